@@ -1,0 +1,34 @@
+"""CPU oracle for the MoE FFN layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+__graft_entry__ and the benchmark's CPU-baseline leg may import or call
+anything in this package.  The product path (the HIP library and its Python
+binding) never does, and shares no code with it.
+
+The oracle is deliberately plain and slow: NumPy in float64, with the layer
+computed the way the adv12 MoE + EPLB tutorial draws it (§3.1): a gate Linear,
+softmax, top-k, renormalisation, then a loop over experts with a boolean mask
+per expert.
+
+Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
+  router_logits        pinned (one-hot closed form, shift invariance)
+  route                pinned (tutorial Q1 worked example, k=1, k=E, identities)
+  bincount             pinned (sum = T*k, tutorial §3.2 total, brute force)
+  capacity             pinned (definition bounds, tutorial Q2 example, skew workload value)
+  capacity_ranks / dispatch   pinned (tutorial Q2 example, brute-force invariants)
+  expert_linear_bias / expert_swiglu   pinned (closed forms)
+  forward              pinned (MOE 学习笔记 combine example, dense brute force,
+                       identical-expert identity, C=0 / shared-only case)
+  stats (imbalance, LPT, naive split, variance)   pinned (tutorial §3.3 / §6 values,
+                       4/3 bound against brute-force OPT)
+  fp8 e4m3 decode      pinned (OCP format values, torch float8_e4m3fn)
+  full-size workloads  parity unpinned beyond the invariants above (the pages
+                       print no outputs for those shapes)
+"""
+from .moe_oracle import (  # noqa: F401
+    widen, router_logits, select_topk, route, route_softmax_of_topk,
+    bincount, capacity, capacity_ranks, dispatch, silu, expert_linear_bias,
+    expert_swiglu, forward, forward_tokens, dense_forward, topk_margin,
+)
+from .stats import expert_imbalance, lpt_pack, naive_split, sample_variance  # noqa: F401
+from .fp8 import e4m3_decode_table, dequant_rows  # noqa: F401

@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test is chosen so that a plausible mistake in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a wrong tie rule) fails it.  No
+expected value here comes from the HIP path.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as mo
+from tests.conftest import GOLDEN
+
+pytestmark = pytest.mark.cpu
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ a2: routing
+def test_renormalisation_page_example():
+    g = _golden("renorm_example.json")
+    p = np.array([g["probs"]])
+    logits = np.log(p).astype(np.float32)          # softmax(log p) = p
+    idx, w = oracle.route(logits, g["k"])
+    assert idx.tolist() == [g["expected_idx"]]
+    exact = [float(Fraction(s)) for s in g["expected_w_exact"]]
+    np.testing.assert_allclose(w[0], exact, rtol=0, atol=1e-7)   # fp32 log rounding
+    np.testing.assert_allclose(np.round(w[0], g["printed_decimals"]), g["expected_w_printed"])
+    assert abs(w.sum() - 1.0) < 1e-15
+
+
+def test_weights_sum_to_one_and_two_formulations_agree():
+    rng = np.random.default_rng(1)
+    for E, k in [(4, 2), (8, 2), (64, 2), (256, 8), (7, 7), (5, 1)]:
+        logits = rng.standard_normal((50, E)).astype(np.float32) * 3
+        idx, w = oracle.route(logits, k)
+        idx2, w2 = oracle.route_softmax_of_topk(logits, k)
+        assert np.array_equal(idx, idx2)
+        np.testing.assert_allclose(w, w2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-12)
+        # weights follow the slot order (slot 0 = largest logit)
+        assert np.all(np.diff(w, axis=1) <= 1e-15)
+
+
+def test_topk_matches_brute_force_and_tie_rule():
+    rng = np.random.default_rng(2)
+    # values from a small grid force many exact ties
+    logits = rng.integers(-3, 4, size=(200, 9)).astype(np.float32)
+    logits[0, :] = 0.0
+    logits[0, 3] = -0.0          # -0.0 ties with +0.0
+    for k in (1, 2, 5, 9):
+        idx = oracle.select_topk(logits, k)
+        for t in range(logits.shape[0]):
+            ref = sorted(range(9), key=lambda e: (-float(logits[t, e]), e))[:k]
+            assert idx[t].tolist() == ref
+    assert oracle.select_topk(logits[:1], 4)[0].tolist() == [0, 1, 2, 3]
+
+
+def test_k1_is_switch_routing_weight_one():
+    # iopenshare §1.2: Switch routing keeps a single expert (argmax); the
+    # renormalised weight of one kept expert is 1.
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((100, 8)).astype(np.float32)
+    idx, w = oracle.route(logits, 1)
+    assert np.array_equal(idx[:, 0], np.argmax(logits, axis=1))
+    assert np.all(w == 1.0)
+
+
+def test_k_equals_E_is_soft_routing():
+    # MOE 学习笔记, 路由策略: soft routing weights every expert by the router's
+    # probability distribution; with k = E nothing is dropped by top-k.
+    from scipy.special import softmax
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((30, 6)).astype(np.float32)
+    idx, w = oracle.route(logits, 6)
+    dense = np.zeros_like(w)
+    np.put_along_axis(dense, idx.astype(np.int64), w, axis=1)
+    np.testing.assert_allclose(dense, softmax(logits.astype(np.float64), axis=1), atol=1e-14)
+
+
+def test_shift_invariance_safe_softmax():
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((40, 8)) * 2
+    a = oracle.route(logits, 2)
+    b = oracle.route(logits + 1000.0, 2)   # would overflow exp without the max shift
+    assert np.array_equal(a[0], b[0])
+    np.testing.assert_allclose(a[1], b[1], atol=1e-9)
+
+
+def test_router_logits_one_hot_closed_form():
+    # x rows that are unit vectors pick out rows of W_g[d, E]; a transposed
+    # W_g or a missing bias fails.
+    d, E = 6, 4
+    rng = np.random.default_rng(6)
+    W_g = rng.standard_normal((d, E)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    x = np.eye(d, dtype=np.float32)
+    np.testing.assert_array_equal(oracle.router_logits(x, W_g), W_g)
+    np.testing.assert_allclose(oracle.router_logits(2 * x, W_g, b), 2 * W_g + b, rtol=1e-7)
+
+
+def test_bf16_widening_definition():
+    # bfloat16 is the upper half of an IEEE binary32: 0x3F80 = 1.0,
+    # 0xC000 = -2.0, 0x3F81 = 1 + 2^-7, 0x0001 = 2^-133 (subnormal).
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F7F], dtype=np.uint16)
+    v = oracle.widen(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 1 + 2.0 ** -7
+    assert v[3] == 2.0 ** -133
+    assert v[4] == (2 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ------------------------------------------------------------------ a3: bincount / capacity
+def test_bincount_sums_to_T_times_k_and_brute_force():
+    g = _golden("lpt_example.json")
+    assert sum(g["load"]) == g["total_routings"] == g["T"] * g["k"]
+    rng = np.random.default_rng(7)
+    for T, E, k in [(64, 4, 2), (300, 16, 3), (1, 8, 8)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        idx, _ = oracle.route(logits, k)
+        c = oracle.bincount(idx, E)
+        assert c.sum() == T * k
+        assert [sum(1 for t in range(T) for j in range(k) if idx[t, j] == e) for e in range(E)] == c.tolist()
+
+
+def test_capacity_definition_bounds():
+    for T, E, k, cf in [(16384, 64, 2, 1.25), (64, 4, 2, 1.25), (4096, 8, 2, 1.0),
+                        (1000, 7, 3, 1.1), (5, 256, 8, 2.0), (64, 4, 2, 0.3125)]:
+        C = oracle.capacity(T, E, k, cf)
+        # C*E/(T*k) is the realised capacity factor: at least cf, less than one
+        # token per expert above it.
+        assert Fraction(C * E, T * k) >= Fraction(cf)
+        assert Fraction(C * E, T * k) < Fraction(cf) + Fraction(E, T * k)
+    assert oracle.capacity(16384, 64, 2, 1.25) == 640
+    assert oracle.capacity(64, 4, 2, None) == -1
+    assert oracle.capacity(64, 4, 2, 0.0) == -1
+
+
+def _idx_with_loads(loads, k, rng):
+    """A [T, k] selection whose bincount is `loads` (each token picks k
+    distinct experts).  Greedy on the largest remaining loads."""
+    loads = list(loads)
+    T = sum(loads) // k
+    rows = []
+    for _ in range(T):
+        order = sorted(range(len(loads)), key=lambda e: (-loads[e], e))[:k]
+        for e in order:
+            loads[e] -= 1
+        rows.append(order)
+    assert all(v == 0 for v in loads)
+    idx = np.array(rows, dtype=np.int32)
+    return idx[rng.permutation(T)]
+
+
+def test_capacity_drop_page_example():
+    g = _golden("capacity_example.json")
+    rng = np.random.default_rng(8)
+    idx = _idx_with_loads(g["load"], 2, rng)
+    w = np.full(idx.shape, 0.5)
+    r = oracle.dispatch(idx, w, 4, g["capacity"])
+    assert r["kept"].tolist() == g["expected_kept"]
+    assert int(r["counts"][0] - r["kept"][0]) == g["expected_overflow_expert0"]
+    # dropped in token order: expert 0's kept tokens are its first 20 tokens
+    toks0 = [t for t in range(idx.shape[0]) if 0 in idx[t]]
+    kept0 = sorted(int(r["perm_token"][p]) for p in range(r["offsets"][0], r["offsets"][1]))
+    assert kept0 == toks0[:20]
+
+
+def test_capacity_large_equals_unlimited_and_zero_drops_all():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((100, 8)).astype(np.float32)
+    idx, w = oracle.route(logits, 2)
+    a = oracle.dispatch(idx, w, 8, -1)
+    b = oracle.dispatch(idx, w, 8, int(a["counts"].max()))
+    for key in ("kept", "offsets", "perm_token", "slot_pos"):
+        assert np.array_equal(a[key], b[key])
+    z = oracle.dispatch(idx, w, 8, 0)
+    assert z["offsets"][-1] == 0 and not z["keep"].any()
+
+
+# ------------------------------------------------------------------ a4: permutation
+def test_dispatch_permutation_invariants():
+    rng = np.random.default_rng(10)
+    for T, E, k, C in [(200, 8, 2, -1), (200, 8, 2, 30), (77, 5, 3, 20), (64, 4, 2, 20)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        logits[:, 0] += 1.0  # skew so the capacity binds
+        idx, w = oracle.route(logits, k)
+        r = oracle.dispatch(idx, w, E, C)
+        P = r["offsets"][-1]
+        # a bijection between kept (t, j) and positions 0..P-1
+        kept_pairs = {(t, j) for t in range(T) for j in range(k) if r["keep"][t, j]}
+        assert len(kept_pairs) == P
+        seen = set()
+        for p in range(P):
+            t, j = int(r["perm_token"][p]), int(r["perm_slot"][p])
+            assert (t, j) in kept_pairs and r["slot_pos"][t, j] == p
+            seen.add((t, j))
+            assert r["perm_w"][p] == w[t, j]
+        assert seen == kept_pairs
+        # sorted by (expert, token)
+        keys = [(int(idx[r["perm_token"][p], r["perm_slot"][p]]), int(r["perm_token"][p])) for p in range(P)]
+        assert keys == sorted(keys)
+        # segment e holds exactly expert e's kept assignments
+        for e in range(E):
+            seg = range(r["offsets"][e], r["offsets"][e + 1])
+            assert all(idx[r["perm_token"][p], r["perm_slot"][p]] == e for p in seg)
+        assert np.all(r["slot_pos"][~r["keep"]] == -1)
+
+
+# ------------------------------------------------------------------ a5/a6/a8: experts and combine
+def test_silu_and_swiglu_closed_form():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(oracle.silu(np.array([1.0, -1.0, 2.0])),
+                               [1 / (1 + math.exp(-1)), -1 / (1 + math.exp(1)), 2 / (1 + math.exp(-2))],
+                               rtol=1e-15)
+    d = 3
+    I = np.eye(d, dtype=np.float32)
+    w = {"W1": I, "W3": 2 * I, "W2": I}
+    X = np.array([[1.0, -1.0, 0.5]])
+    Y = oracle.expert_swiglu(X, w)
+    # silu applies to the W1 product, the W3 product is the linear gate
+    ref = oracle.silu(X) * (2 * X)
+    np.testing.assert_allclose(Y, ref, rtol=1e-15)
+    assert not np.allclose(Y, oracle.silu(2 * X) * X)
+    # W2 maps d_ff back to d and is stored [out, in]
+    W2 = np.array([[0, 1, 0], [0, 0, 1], [1, 0, 0]], dtype=np.float32)
+    Y2 = oracle.expert_swiglu(X, {"W1": I, "W3": 2 * I, "W2": W2})
+    np.testing.assert_allclose(Y2[0], ref[0][[1, 2, 0]], rtol=1e-15)
+
+
+def test_linear_bias_expert_closed_form():
+    W = np.array([[1, 2], [3, 4]], dtype=np.float32)    # [out, in]
+    b = np.array([0.5, -0.5], dtype=np.float32)
+    Y = oracle.expert_linear_bias(np.array([[1.0, 0.0], [0.0, 1.0]]), {"W": W, "b": b})
+    np.testing.assert_allclose(Y, [[1.5, 2.5], [2.5, 3.5]])
+
+
+def test_combine_page_example():
+    g = _golden("combine_example.json")
+    outs = np.array(g["expert_outputs"], dtype=np.float32)
+    wts = g["weights"]
+    # two experts whose output ignores x (W = 0, bias = the printed output)
+    experts = [{"W": np.zeros((2, 2), np.float32), "b": outs[e]} for e in range(2)]
+    W_g = np.zeros((2, 2), np.float32)
+    b_g = np.log(np.array(wts)).astype(np.float32)   # softmax(b_g) = (0.7, 0.3)
+    x = np.ones((1, 2), np.float32)
+    r = oracle.forward(x, W_g, b_g, 2, 2, lambda e: experts[e], kind="linear_bias")
+    np.testing.assert_allclose(r["y"][0], g["expected"], atol=1e-7)
+    # swapping which weight goes with which expert would give [0.41, 0.33]
+    assert abs(r["y"][0, 0] - 0.41) > 0.1
+
+
+def _tiny_swiglu(T, d, E, d_ff, seed, shared=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    W_g = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    ex = [{"W1": (rng.standard_normal((d_ff, d)) / np.sqrt(d)).astype(np.float32),
+           "W3": (rng.standard_normal((d_ff, d)) / np.sqrt(d)).astype(np.float32),
+           "W2": (rng.standard_normal((d, d_ff)) / np.sqrt(d_ff)).astype(np.float32)}
+          for _ in range(E)]
+    sh = None
+    if shared:
+        sh = {"W1": (rng.standard_normal((d_ff, d)) / np.sqrt(d)).astype(np.float32),
+              "W3": (rng.standard_normal((d_ff, d)) / np.sqrt(d)).astype(np.float32),
+              "W2": (rng.standard_normal((d, d_ff)) / np.sqrt(d_ff)).astype(np.float32)}
+    return x, W_g, ex, sh
+
+
+@pytest.mark.parametrize("T,d,E,k,d_ff,C,shared", [
+    (40, 8, 4, 2, 12, -1, False), (40, 8, 4, 2, 12, 9, False),
+    (33, 6, 8, 3, 10, 7, True), (20, 5, 6, 6, 4, -1, False), (25, 4, 5, 1, 3, 4, True)])
+def test_masked_loop_equals_dense_brute_force(T, d, E, k, d_ff, C, shared):
+    x, W_g, ex, sh = _tiny_swiglu(T, d, E, d_ff, seed=T * 7 + E, shared=shared)
+    shf = (lambda: sh) if shared else None
+    r = oracle.forward(x, W_g, None, k, E, lambda e: ex[e], C=C, shared=shf)
+    yd = oracle.dense_forward(x, W_g, None, k, E, lambda e: ex[e], C=C, shared=shf)
+    np.testing.assert_allclose(r["y"], yd, rtol=0, atol=1e-12)
+
+
+def test_identical_experts_give_the_expert_itself():
+    # weights of a token sum to 1, so with identical experts y = expert(x)
+    x, W_g, ex, _ = _tiny_swiglu(50, 8, 6, 16, seed=11)
+    r = oracle.forward(x, W_g, None, 3, 6, lambda e: ex[0])
+    np.testing.assert_allclose(r["y"], oracle.expert_swiglu(x.astype(np.float64), ex[0]), atol=1e-12)
+
+
+def test_token_permutation_equivariance_and_expert_relabelling():
+    x, W_g, ex, _ = _tiny_swiglu(30, 8, 5, 12, seed=12)
+    base = oracle.forward(x, W_g, None, 2, 5, lambda e: ex[e])["y"]
+    perm = np.random.default_rng(0).permutation(30)
+    yp = oracle.forward(x[perm], W_g, None, 2, 5, lambda e: ex[e])["y"]
+    np.testing.assert_allclose(yp, base[perm], atol=1e-12)
+    rel = np.array([3, 0, 4, 1, 2])                # new expert e' = rel[e]
+    inv = np.argsort(rel)
+    W_g2 = np.empty_like(W_g)
+    W_g2[:, rel] = W_g
+    y2 = oracle.forward(x, W_g2, None, 2, 5, lambda e: ex[inv[e]])["y"]
+    np.testing.assert_allclose(y2, base, atol=1e-12)
+
+
+def test_capacity_zero_leaves_only_the_shared_expert():
+    x, W_g, ex, sh = _tiny_swiglu(20, 8, 4, 8, seed=13, shared=True)
+    r = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=0, shared=lambda: sh)
+    np.testing.assert_allclose(r["y"], oracle.expert_swiglu(x.astype(np.float64), sh), atol=1e-14)
+    r0 = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=0)
+    assert np.all(r0["y"] == 0)
+
+
+def test_forward_tokens_equals_forward():
+    x, W_g, ex, sh = _tiny_swiglu(60, 8, 6, 8, seed=14, shared=True)
+    b = np.linspace(0, -3, 6).astype(np.float32)
+    full = oracle.forward(x, W_g, b, 2, 6, lambda e: ex[e], C=15, shared=lambda: sh)
+    toks = [0, 5, 59, 33]
+    yr, _ = oracle.forward_tokens(toks, x, W_g, b, 2, 6, lambda e: ex[e], C=15, shared=lambda: sh)
+    np.testing.assert_allclose(yr, full["y"][toks], atol=1e-13)
+
+
+def test_idx_override_recomputes_weights_and_capacity():
+    x, W_g, ex, _ = _tiny_swiglu(30, 8, 4, 8, seed=15)
+    r = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=8)
+    o = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=8, idx_override=r["idx"])
+    np.testing.assert_allclose(o["y"], r["y"], atol=0)
+    alt = r["idx"].copy()
+    alt[0] = alt[0][::-1]                       # swap slot order: same set, same y
+    o2 = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=8, idx_override=alt)
+    np.testing.assert_allclose(o2["y"], r["y"], atol=1e-14)
+
+
+def test_topk_margin():
+    l = np.array([[3.0, 1.0, 2.0, 0.5]], np.float32)
+    assert oracle.topk_margin(l, 1)[0] == 1.0          # 3 - 2
+    assert oracle.topk_margin(l, 2)[0] == 1.0          # min(1, 1)
+    assert oracle.topk_margin(l, 3)[0] == 0.5          # min(1, 1, 0.5)
+    assert oracle.topk_margin(l, 4)[0] == 0.5          # k = E: last gap skipped
+
+
+# ------------------------------------------------------------------ a9: load stats
+def test_lpt_page_example():
+    g = _golden("lpt_example.json")
+    a, dev = oracle.lpt_pack(g["load"], g["devices"])
+    assert a.tolist() == g["lpt_assignment"]
+    assert dev.tolist() == g["lpt_device_load"]
+    naive = oracle.naive_split(g["load"], g["devices"])
+    assert naive.tolist() == g["naive_device_load"]
+    assert oracle.sample_variance(naive) == g["naive_variance"]
+    assert oracle.sample_variance(dev) == g["lpt_variance"]
+    assert round(oracle.expert_imbalance(g["load"]), 3) == g["imbalance_printed"]
+    assert max(dev) == g["optimum_max_load"]
+
+
+def _opt_makespan(load, D):
+    best = None
+    for assign in itertools.product(range(D), repeat=len(load)):
+        bins = [0] * D
+        for e, dv in enumerate(assign):
+            bins[dv] += load[e]
+        m = max(bins)
+        best = m if best is None else min(best, m)
+    return best
+
+
+def test_lpt_four_thirds_bound_against_brute_force():
+    rng = np.random.default_rng(16)
+    for _ in range(60):
+        E = int(rng.integers(2, 9))
+        D = int(rng.integers(2, 4))
+        load = rng.integers(0, 50, size=E).tolist()
+        _, dev = oracle.lpt_pack(load, D)
+        assert sum(dev) == sum(load)
+        opt = _opt_makespan(load, D)
+        assert max(dev) <= Fraction(4, 3) * opt + 0   # classical LPT bound
+    # a tight-ish instance of the bound: 2 machines, loads 3,3,2,2,2 -> LPT 7, OPT 6
+    _, dev = oracle.lpt_pack([3, 3, 2, 2, 2], 2)
+    assert max(dev) == 7 and _opt_makespan([3, 3, 2, 2, 2], 2) == 6
+
+
+def test_imbalance_epsilon_guards_empty_expert():
+    assert oracle.expert_imbalance([5, 0, 3]) == pytest.approx(5 / 1e-6)
+    assert oracle.expert_imbalance([4, 4]) == pytest.approx(1.0, abs=1e-6)
+
+
+# ------------------------------------------------------------------ fp8 e4m3
+def test_e4m3_table_against_format_definition_and_torch():
+    t = oracle.e4m3_decode_table()
+    assert t[0x38] == 1.0 and t[0xB8] == -1.0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and math.copysign(1, t[0x80]) == -1
+    finite = t[~np.isnan(t)]
+    assert finite.max() == 448.0
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)                  # monotone over positive codes
+    import torch
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both = ~np.isnan(t)
+    assert np.array_equal(np.isnan(ref), ~both)
+    assert np.array_equal(ref[both], t[both])
+
+
+def test_dequant_rows_group_scaling():
+    codes = np.full((256, 3), 0x38, dtype=np.uint8)        # all 1.0
+    s = np.array([0.5, 4.0], np.float32)
+    W = oracle.dequant_rows(codes, s)
+    assert np.all(W[:128] == 0.5) and np.all(W[128:] == 4.0)

@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP translation units of the library.
+// Not part of the public ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDispatchChunk = 1024;  // assignments per histogram / rank chunk
+constexpr int kFp8Group = 128;        // output features per fp8 scale
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- workspace
+struct WsLayout {
+  int router_splits;     // split-K factor of the router GEMM
+  int nchunks;           // dispatch chunks of kDispatchChunk assignments
+  int64_t P_max;         // upper bound of kept assignments
+  int64_t H_rows;        // rows of the hidden buffer (P_max + T for a shared expert)
+  size_t off_partial;    // fp32 [router_splits, T, E]
+  size_t off_chunk_hist; // int32 [nchunks, E]
+  size_t off_chunk_base; // int32 [nchunks, E]
+  size_t off_perm_token; // int32 [P_max]
+  size_t off_perm_w;     // fp32  [P_max]
+  size_t off_slot_pos;   // int32 [T*k]
+  size_t off_H;          // bf16  [H_rows, d_ff]
+  size_t total;
+};
+
+WsLayout ws_layout(const moe_shape& s);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All are asynchronous.
+hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
+                              float* partial, int splits, hipStream_t st);
+hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
+                       const float* b_g, float* logits, int32_t* topk_idx,
+                       float* topk_w, hipStream_t st);
+
+hipError_t launch_dispatch(const moe_shape& s, const WsLayout& L,
+                           const int32_t* topk_idx, const float* topk_w,
+                           int32_t* counts, int32_t* offsets, uint8_t* keep,
+                           int32_t* perm_token, float* perm_w, int32_t* slot_pos,
+                           int32_t* chunk_hist, int32_t* chunk_base, hipStream_t st);
+hipError_t launch_gather(const moe_shape& s, int64_t P_max, const int32_t* offsets,
+                         const int32_t* perm_token, const void* x, void* x_perm,
+                         hipStream_t st);
+
+hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t st);
+
+hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L,
+                             const moe_weights& w, const void* x,
+                             const int32_t* offsets, const int32_t* perm_token,
+                             const float* perm_w, float* y_perm, float* y,
+                             void* H, hipStream_t st, hipEvent_t ev_mid = nullptr);
+
+hipError_t launch_combine(const moe_shape& s, const float* y_perm,
+                          const int32_t* slot_pos, const float* topk_w, float* y,
+                          hipStream_t st);
+
+}  // namespace moe

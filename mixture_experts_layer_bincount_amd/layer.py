@@ -1,0 +1,45 @@
+"""MoELayer: device buffers plus one moe_forward call per batch.
+
+The layer of the adv12 MoE + EPLB tutorial §4.1 (MoELayer(d_model,
+num_experts, top_k) returning the output and the per-expert load), holding
+caller-provided device weights.  All compute happens in the HIP library.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (DT_BF16, DT_F32, DT_FP8_E4M3, LINEAR_BIAS, SWIGLU, make_shape, make_weights,
+               moe_forward, moe_workspace_bytes)
+
+
+class MoELayer:
+    """Forward pass of one MoE FFN layer on the current HIP device.
+
+    weights: dict of device tensors named as in moe.h (W1, W3, W2 [, s1, s3,
+    s2] [, W1s, W3s, W2s [, s1s, s3s, s2s]] for SwiGLU; W, b for Linear+bias).
+    """
+
+    def __init__(self, T, d, E, top_k, d_ff, *, W_g, b_g=None, weights, capacity=-1,
+                 kind="swiglu", w_dtype="bf16", has_shared=False, device="cuda"):
+        self.kind = SWIGLU if kind == "swiglu" else LINEAR_BIAS
+        act = DT_BF16 if self.kind == SWIGLU else DT_F32
+        wdt = {"bf16": DT_BF16, "fp8_e4m3": DT_FP8_E4M3, "f32": DT_F32}[w_dtype]
+        self.shape = make_shape(T, d, E, top_k, d_ff, capacity, act, wdt, self.kind, has_shared)
+        self.W_g = W_g
+        self.b_g = b_g
+        self.weights = make_weights(**weights)
+        dev = torch.device(device)
+        self.ws = torch.empty(max(moe_workspace_bytes(self.shape), 256), dtype=torch.uint8,
+                              device=dev)
+        self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+
+    def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        moe_forward(self.shape, x, self.W_g, self.b_g, self.weights, self.y, self.topk_idx,
+                    self.topk_w, self.counts, self.offsets, self.ws, stream)
+        return self.y
+
+    __call__ = forward

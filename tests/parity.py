@@ -1,0 +1,95 @@
+"""Helpers that run the HIP path through the C ABI and compare it with the oracle.
+
+Used by the GPU tests, the smoke check and the benchmark's parity line.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from moe_synth import Workload
+
+MARGIN_EXCLUDE = 1e-5            # tokens with a smaller top-k margin may flip
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_e4m3": 6e-2}
+
+
+def tolerance(cfg) -> float:
+    return TOL["f32"] if cfg.kind == "linear_bias" else TOL[cfg.w]
+
+
+def oracle_capacity(cfg) -> int:
+    return oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.cf)
+
+
+def gpu_forward(wl: Workload, dev=None):
+    """Run moe_forward once on the workload; returns (numpy outputs, layer, dev)."""
+    import torch
+
+    import mixture_experts_layer_bincount_amd as moe
+    from moe_synth.device import upload
+    c = wl.cfg
+    if dev is None:
+        dev = upload(wl)
+    cap = moe.moe_capacity(c.T, c.E, c.k, c.cf) if c.cf else -1
+    layer = moe.MoELayer(c.T, c.d, c.E, c.k, c.d_ff, W_g=dev["W_g"], b_g=dev["b_g"],
+                         weights=dev["weights"], capacity=cap, kind=c.kind, w_dtype=c.w,
+                         has_shared=c.shared)
+    layer(dev["x"])
+    torch.cuda.synchronize()
+    out = dict(y=layer.y.cpu().numpy(), idx=layer.topk_idx.cpu().numpy(),
+               w=layer.topk_w.cpu().numpy(), counts=layer.counts.cpu().numpy(),
+               offsets=layer.offsets.cpu().numpy())
+    return out, layer, dev
+
+
+def check_routing(logits, k, gpu_idx, gpu_w, w_tol=1e-5):
+    """Indices equal except on tokens whose top-k margin is below 1e-5; weights
+    of the equal tokens within w_tol.  Returns the mask of flipped tokens."""
+    o_idx, o_w = oracle.route(logits, k)
+    margin = oracle.topk_margin(logits, k)
+    flip = (gpu_idx != o_idx).any(axis=1)
+    bad = flip & (margin >= MARGIN_EXCLUDE)
+    assert not bad.any(), (f"{bad.sum()} tokens with margin >= {MARGIN_EXCLUDE} routed "
+                           f"differently, first {np.nonzero(bad)[0][:5]}")
+    same = ~flip
+    if same.any():
+        err = np.abs(gpu_w[same] - o_w[same]).max()
+        assert err <= w_tol, f"routing weights differ by {err}"
+    return flip
+
+
+def rel_err(y, y_ref) -> float:
+    rms = float(np.sqrt(np.mean(np.square(y_ref))))
+    return float(np.abs(y - y_ref).max() / max(rms, 1e-30))
+
+
+def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None) -> dict:
+    """Compare one moe_forward result with the oracle (on all tokens, or on
+    the sampled `tokens`).  Returns a report dict."""
+    c = wl.cfg
+    C = oracle_capacity(c)
+    x = wl.x()
+    W_g = wl.W_g()
+    b_g = wl.b_g()
+    logits = oracle.router_logits(x, W_g, b_g)
+    flip = check_routing(logits, c.k, gpu["idx"], gpu["w"])
+    override = gpu["idx"] if flip.any() else None
+    shared = wl.shared if c.shared else None
+    if tokens is None:
+        r = oracle.forward(x, W_g, b_g, c.k, c.E, wl.expert, kind=c.kind, C=C,
+                           shared=shared, idx_override=override, logits=logits)
+        y_ref = r["y"]
+        y = gpu["y"]
+    else:
+        tokens = np.asarray(tokens)
+        y_ref, r = oracle.forward_tokens(tokens, x, W_g, b_g, c.k, c.E, wl.expert, kind=c.kind,
+                                         C=C, shared=shared, idx_override=override)
+        y = gpu["y"][tokens]
+    # load accounting is bit-exact given the same selection
+    assert np.array_equal(gpu["counts"], r["counts"]), "counts differ"
+    assert np.array_equal(gpu["offsets"], r["offsets"]), "offsets differ"
+    err = rel_err(y, y_ref)
+    tol = tolerance(c) if tol is None else tol
+    assert err <= tol, f"max-abs-err/RMS = {err:.3e} > {tol}"
+    return dict(err=err, flipped=int(flip.sum()), tol=tol, kept=int(r["offsets"][-1]),
+                counts=r["counts"])

@@ -1,0 +1,103 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, its host statistics agree with the oracle, and argument validation
+rejects bad calls before any GPU work (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import ROOT
+
+pytestmark = pytest.mark.cpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_layer_bincount_amd as m
+    return m
+
+
+def test_library_exports_every_declared_symbol(moe):
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(moe_[a-z_]+)\s*\(", hdr, re.M))
+    assert declared == set(moe.EXPORTS), declared ^ set(moe.EXPORTS)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_capacity_matches_oracle(moe):
+    rng = np.random.default_rng(0)
+    cases = [(16384, 64, 2, 1.25), (64, 4, 2, 1.25), (4096, 8, 2, 1.0), (64, 4, 2, None),
+             (0, 8, 2, 1.25), (1, 256, 8, 0.01)]
+    for _ in range(200):
+        cases.append((int(rng.integers(1, 50000)), int(rng.integers(1, 300)),
+                      int(rng.integers(1, 9)), float(rng.uniform(0.1, 3.0))))
+    for T, E, k, cf in cases:
+        assert moe.moe_capacity(T, E, k, cf) == oracle.capacity(T, E, k, cf), (T, E, k, cf)
+    assert moe.moe_capacity(-1, 4, 2, 1.0) == -2
+
+
+def test_lpt_and_imbalance_match_oracle(moe):
+    a, b = moe.moe_lpt_pack([38, 34, 29, 27], 2)
+    assert a == [0, 1, 1, 0] and b == [65, 63]
+    assert round(moe.moe_load_imbalance([38, 34, 29, 27]), 3) == 1.407
+    rng = np.random.default_rng(1)
+    for _ in range(100):
+        E = int(rng.integers(1, 300))
+        D = int(rng.integers(1, 17))
+        load = rng.integers(0, 1000, size=E)
+        load[rng.random(E) < 0.2] = 0
+        a, b = moe.moe_lpt_pack(load.tolist(), D)
+        oa, ob = oracle.lpt_pack(load, D)
+        assert a == oa.tolist() and b == ob.tolist()
+        assert moe.moe_load_imbalance(load.tolist()) == pytest.approx(oracle.expert_imbalance(load), rel=1e-15)
+
+
+def test_workspace_bytes(moe):
+    s = moe.make_shape(4096, 4096, 8, 2, 14336)
+    n = moe.moe_workspace_bytes(s)
+    # at least the hidden buffer of 8192 grouped rows in bf16
+    assert n >= 8192 * 14336 * 2
+    assert moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 0, 2, 14336)) == 0
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(T=-1), "T="), (dict(E=0), "E="), (dict(top_k=9), "top_k"), (dict(top_k=0), "top_k"),
+    (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 256"),
+    (dict(d_ff=100), "d_ff"), (dict(act_dtype=0), "bf16 x"), (dict(w_dtype=0), "weights"),
+    (dict(kind=7), "kind")])
+def test_validation_rejects_bad_shapes(moe, kw, needle):
+    base = dict(T=16, d=256, E=8, top_k=2, d_ff=128, capacity=-1, act_dtype=1, w_dtype=1,
+                kind=1, has_shared=False)
+    base.update(kw)
+    s = moe.make_shape(**base)
+    fake = 256  # never dereferenced: validation fails first
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(s, fake, fake, None, moe.make_weights(W1=fake, W3=fake, W2=fake), fake,
+                        fake, fake, fake, fake, fake, stream=0)
+    assert ei.value.status in (1, 2)
+    assert needle in str(ei.value)
+
+
+def test_validation_null_and_alignment(moe):
+    s = moe.make_shape(16, 256, 8, 2, 128)
+    with pytest.raises(moe.MoEError, match="x is NULL"):
+        moe.moe_forward(s, None, 256, None, moe.make_weights(W1=256, W3=256, W2=256), 256, 256,
+                        256, 256, 256, 256, stream=0)
+    with pytest.raises(moe.MoEError, match="aligned"):
+        moe.moe_forward(s, 258, 256, None, moe.make_weights(W1=256, W3=256, W2=256), 256, 256,
+                        256, 256, 256, 256, stream=0)
+    with pytest.raises(moe.MoEError, match="exactly one"):
+        moe.moe_expert_ffn(s, moe.make_weights(W1=256, W3=256, W2=256), 256, 256, 256, 256,
+                           None, None, 256, stream=0)
+    with pytest.raises(moe.MoEError, match="E <= 256"):
+        moe.moe_route(moe.make_shape(16, 256, 512, 2, 128), 256, 256, None, None, 256, 256, 256,
+                      stream=0)
+    with pytest.raises(moe.MoEError, match="shared"):
+        moe.moe_forward(moe.make_shape(16, 8, 4, 2, 0, -1, 0, 0, 0, True), 256, 256, None,
+                        moe.make_weights(W=256, b=256), 256, 256, 256, 256, 256, 256, stream=0)

@@ -1,0 +1,134 @@
+"""GPU parity of the routing and dispatch stages against the oracle.
+
+Routing from given logits and dispatch from given selections must be
+bit-exact; the fused router may only change the selection of tokens whose
+top-k margin is below 1e-5.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from moe_synth import Workload, custom_config
+from tests.parity import check_routing
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_layer_bincount_amd as m
+    return m
+
+
+def _logits(T, E, seed, ties=False):
+    rng = np.random.default_rng(seed)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        l[: T // 2] = np.round(l[: T // 2] * 2) / 2     # many exact ties
+        l[0, :] = 0.0
+        l[0, 1::2] = -0.0
+    return l
+
+
+@pytest.mark.parametrize("T,E,k,ties", [
+    (64, 4, 2, False), (1000, 8, 2, True), (777, 64, 2, True), (500, 256, 8, True),
+    (300, 16, 16, True), (33, 128, 5, False), (1, 1, 1, False), (129, 1024, 32, True),
+    (4096, 8, 1, False), (70, 3, 3, True)])
+def test_route_from_logits_bit_exact(moe, T, E, k, ties):
+    print(f"[route_from_logits] T={T} E={E} k={k} ties={ties}", flush=True)
+    l = _logits(T, E, seed=T + 31 * E + k, ties=ties)
+    s = moe.make_shape(T, 256, E, k)
+    dl = torch.from_numpy(l).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route_from_logits(s, dl, idx, w)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route(l, k)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("T,d,E,k,act,bias", [
+    (64, 8, 4, 2, "f32", False), (1000, 512, 64, 2, "bf16", True),
+    (300, 1024, 256, 8, "bf16", False), (64, 4096, 8, 2, "bf16", False),
+    (517, 256, 8, 2, "bf16", True), (1, 256, 16, 4, "bf16", False)])
+def test_route_fused(moe, T, d, E, k, act, bias):
+    print(f"[route] T={T} d={d} E={E} k={k} act={act}", flush=True)
+    kind = "linear_bias" if act == "f32" else "swiglu"
+    cfg = custom_config(T, d, E, k, 128, kind=kind, act=act, w="f32" if act == "f32" else "bf16",
+                        router_bias="zipf1.5" if bias else None, seed=T * 7 + E)
+    wl = Workload(cfg)
+    from moe_synth.device import to_device
+    x = wl.x()
+    W_g = wl.W_g()
+    b_g = wl.b_g()
+    dx = to_device(x, "cuda")
+    dW = torch.from_numpy(W_g).cuda()
+    db = torch.from_numpy(b_g).cuda() if b_g is not None else None
+    s = moe.make_shape(T, d, E, k, 128, -1, moe.DT_F32 if act == "f32" else moe.DT_BF16,
+                       moe.DT_F32 if act == "f32" else moe.DT_BF16,
+                       moe.LINEAR_BIAS if act == "f32" else moe.SWIGLU)
+    ws = moe.workspace(s)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, dx, dW, db, logits, idx, w, ws)
+    torch.cuda.synchronize()
+    o_logits = oracle.router_logits(x, W_g, b_g)
+    g_logits = logits.cpu().numpy()
+    assert np.abs(g_logits - o_logits).max() <= 2e-5 * (1 + np.abs(o_logits).max())
+    check_routing(o_logits, k, idx.cpu().numpy(), w.cpu().numpy(), w_tol=1e-5)
+    # the selection is a pure function of the logits the kernel produced
+    o_idx2, _ = oracle.route(g_logits, k)
+    assert np.array_equal(idx.cpu().numpy(), o_idx2)
+
+
+def _skewed_selection(T, E, k, seed, skew):
+    rng = np.random.default_rng(seed)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l += (skew * np.log(1.0 / (np.arange(E) + 1.0))).astype(np.float32)
+    return oracle.route(l, k)
+
+
+@pytest.mark.parametrize("T,E,k,C,skew", [
+    (64, 4, 2, -1, 0.0), (64, 4, 2, 20, 0.0), (5000, 8, 2, -1, 0.0), (5000, 8, 2, 900, 1.0),
+    (3000, 64, 2, 100, 1.5), (16384, 64, 2, 640, 1.5), (4096, 256, 8, -1, 0.0),
+    (700, 256, 8, 10, 2.0), (1, 8, 2, -1, 0.0), (513, 16, 4, 0, 0.0), (999, 1024, 32, 40, 0.5)])
+def test_dispatch_bit_exact(moe, T, E, k, C, skew):
+    print(f"[dispatch] T={T} E={E} k={k} C={C}", flush=True)
+    o_idx, o_w = _skewed_selection(T, E, k, seed=T + E, skew=skew)
+    o_w32 = o_w.astype(np.float32)
+    r = oracle.dispatch(o_idx, o_w32, E, C)
+    d = 64
+    s = moe.make_shape(T, d, E, k, 128, C)
+    ws = moe.workspace(s)
+    A = T * k
+    P_max = A if C < 0 else min(A, E * C)
+    rng = np.random.default_rng(0)
+    x = rng.integers(0, 1 << 16, size=(T, d), dtype=np.uint16)
+    dx = torch.from_numpy(x.view(np.int16)).cuda()
+    didx = torch.from_numpy(o_idx).cuda()
+    dw = torch.from_numpy(o_w32).cuda()
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    keep = torch.full((A,), 7, dtype=torch.uint8, device="cuda")
+    perm_token = torch.full((max(P_max, 1),), -7, dtype=torch.int32, device="cuda")
+    perm_w = torch.full((max(P_max, 1),), -7.0, dtype=torch.float32, device="cuda")
+    slot_pos = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros((max(P_max, 1), d), dtype=torch.int16, device="cuda")
+    moe.moe_dispatch(s, didx, dw, dx, counts, offsets, keep, perm_token, perm_w, slot_pos,
+                     x_perm, ws)
+    torch.cuda.synchronize()
+    P = int(r["offsets"][-1])
+    assert np.array_equal(counts.cpu().numpy(), r["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), r["offsets"])
+    assert np.array_equal(keep.cpu().numpy().astype(bool), r["keep"].ravel())
+    assert np.array_equal(slot_pos.cpu().numpy(), r["slot_pos"].ravel())
+    assert np.array_equal(perm_token.cpu().numpy()[:P], r["perm_token"])
+    assert np.array_equal(perm_w.cpu().numpy()[:P], r["perm_w"].astype(np.float32))
+    xp = x_perm.cpu().numpy().view(np.uint16)[:P]
+    assert np.array_equal(xp, x[r["perm_token"]])

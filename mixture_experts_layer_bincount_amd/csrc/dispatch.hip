@@ -171,7 +171,7 @@ hipError_t launch_gather(const moe_shape& s, int64_t P_max, const int32_t* offse
                          const int32_t* perm_token, const void* x, void* x_perm,
                          hipStream_t st) {
   const int64_t row_bytes = (int64_t)s.d * (s.act_dtype == MOE_DT_F32 ? 4 : 2);
-  const int64_t total = P_max * row_bytes;
+  if (P_max <= 0) return hipSuccess;  // nothing can be kept
   if (row_bytes % 16 == 0) {
     const int vpr = (int)(row_bytes / 16);
     const int64_t n = P_max * vpr;
@@ -186,7 +186,6 @@ hipError_t launch_gather(const moe_shape& s, int64_t P_max, const int32_t* offse
                                                      (const uint32_t*)x, (uint32_t*)x_perm,
                                                      P_max, vpr);
   }
-  (void)total;
   return hipGetLastError();
 }
 

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 template <int MODE, bool FP8>
 hipError_t launch_gemm(const GemmParams& p, int64_t mtiles_max, int ntiles, hipStream_t st) {
+  if (mtiles_max <= 0 || ntiles <= 0) return hipSuccess;
   dim3 grid((unsigned)ntiles, (unsigned)mtiles_max);
   grouped_gemm_kernel<MODE, FP8><<<grid, 256, 0, st>>>(p);
   return hipGetLastError();

@@ -96,6 +96,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -134,6 +136,13 @@ def main() -> int:
     for _ in range(args.warmup):
         layer(x)
     torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- timed region: K steps, stage events recorded on the launch stream
     moe.moe_timing_enable(True)

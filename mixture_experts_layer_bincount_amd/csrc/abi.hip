@@ -52,9 +52,17 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     if (s->w_dtype != MOE_DT_BF16 && s->w_dtype != MOE_DT_FP8_E4M3)
       return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts need bf16 or fp8-e4m3 weights");
     if (need_ffn) {
-      if (s->d % 256 != 0) return fail(MOE_ERR_INVALID, "d=%d must be a multiple of 256", s->d);
+      if (s->d % 64 != 0) return fail(MOE_ERR_INVALID, "d=%d must be a multiple of 64", s->d);
       if (s->d_ff <= 0 || s->d_ff % 128 != 0)
         return fail(MOE_ERR_INVALID, "d_ff=%d must be a positive multiple of 128", s->d_ff);
+      // the grouped GEMM addresses each operand with 32-bit byte offsets
+      const int64_t lim = ((int64_t)1 << 31) - 1;
+      const int64_t A = s->T * (int64_t)s->top_k;
+      const int64_t P_max = s->capacity < 0 ? A : std::min<int64_t>(A, (int64_t)s->E * s->capacity);
+      const int64_t H_rows = P_max + (s->has_shared ? s->T : 0);
+      if (s->T * (int64_t)s->d * 2 > lim || H_rows * (int64_t)s->d_ff * 2 > lim ||
+          (int64_t)s->d * s->d_ff * 2 > lim)
+        return fail(MOE_ERR_UNSUPPORTED, "an operand exceeds 2 GiB (x, hidden rows or one expert matrix)");
     }
     if (s->d % 8 != 0) return fail(MOE_ERR_INVALID, "d=%d must be a multiple of 8", s->d);
   } else if (s->kind == MOE_EXPERT_LINEAR_BIAS) {

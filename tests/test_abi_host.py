@@ -68,7 +68,7 @@ def test_workspace_bytes(moe):
 
 @pytest.mark.parametrize("kw,needle", [
     (dict(T=-1), "T="), (dict(E=0), "E="), (dict(top_k=9), "top_k"), (dict(top_k=0), "top_k"),
-    (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 256"),
+    (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 64"),
     (dict(d_ff=100), "d_ff"), (dict(act_dtype=0), "bf16 x"), (dict(w_dtype=0), "weights"),
     (dict(kind=7), "kind")])
 def test_validation_rejects_bad_shapes(moe, kw, needle):

@@ -31,6 +31,11 @@
 // operands in that XCD's L2.  The down projection may split K across
 // workgroups when the tile grid is small (decode); partial sums are added
 // by the same atomics.
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,12 +45,22 @@ enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_DOWN_PERM = 2 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;       // activation rows per tile
-constexpr int BNB = 512;      // weight rows per tile
+// Tile shapes: BM activation rows x BNB weight rows with BM * BNB = 65536
+// (four waves of 128 x 128): 128 x 512 (waves split the weight rows) or
+// 256 x 256 (2 x 2 waves).
 constexpr int BK = 32;        // K per step
 constexpr int LDSK = BK + 8;  // padded LDS row, bf16 elements (80 bytes)
-constexpr int A_STAGE = BM * LDSK;
-constexpr int B_STAGE = BNB * LDSK;
+template <int BM>
+struct Tile {
+  static constexpr int BNB = 65536 / BM;     // weight rows per tile
+  static constexpr int WM = BM / 128;        // waves along the activation rows
+  static constexpr int WN = 4 / WM;          // waves along the weight rows
+  static constexpr int NA = BM / 64;         // 16-byte A loads per thread and K step
+  static constexpr int NB = BNB / 64;        // 16-byte B loads per thread and K step
+  static constexpr int A_STAGE = BM * LDSK;
+  static constexpr int B_STAGE = BNB * LDSK;
+  static constexpr size_t LDS = (size_t)2 * (A_STAGE + B_STAGE) * sizeof(uint16_t);
+};
 constexpr int GROUP_M = 8;    // row tiles per XCD block
 constexpr int GROUP_N = 4;    // weight tiles per XCD block
 constexpr int NUM_XCD = 8;
@@ -76,6 +91,8 @@ struct GemmParams {
   int mt_max;                 // row-tile slots in the grid
   int nt;                     // weight tiles
   int ksplit;                 // K ranges (DOWN only)
+  int krot;                   // rotate each workgroup's K order (spreads L2 channels)
+  int cache_aux;              // cache-policy bits of the operand loads
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -99,7 +116,27 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
   return s | (e ? normal : sub);
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at
+// compile time.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor word 3
+
+// A raw buffer resource over [ptr, ptr + bytes) built from values the caller
+// knows to be wave-uniform, pinned to scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* ptr, int64_t bytes) {
+  const uint64_t a = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3);
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -125,21 +162,29 @@ __device__ __forceinline__ uint4 load_b8(__amdgpu_buffer_rsrc_t r, uint32_t voff
   }
 }
 
-template <int MODE, bool FP8>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* As = lds;                    // [2][BM][LDSK]
-  uint16_t* Bs = lds + 2 * A_STAGE;      // [2][BNB][LDSK]
+// Where a workgroup's tile lies: expert segment, rows, weight tile, K range.
+struct TileMap {
+  int e;         // expert (E = the shared expert)
+  int m0;        // first row of the tile within the expert's segment
+  int rows;      // rows in the expert's segment
+  int seg;       // first grouped row of the segment (routed experts)
+  int ntile;     // weight tile
+  int kbeg, nk;  // K steps of this workgroup
+  bool shared_e;
+};
+
+// XCD-aware tile order, then the row-tile slot -> (expert, first row) map
+// read from the device-side offsets.  Returns false when the workgroup has
+// no tile.  Must be called by all threads of the workgroup.
+template <int MODE, int BM>
+__device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   __shared__ int s_scan[4];
-  __shared__ int s_e, s_m0, s_rows, s_seg;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // ---- XCD-aware tile order.  Workgroup ids are dealt round-robin to the 8
-  // XCDs; give each XCD a contiguous range of logical tiles, ordered in
-  // GROUP_M x GROUP_N blocks (row-tile groups fastest).
+  __shared__ int s_info[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous range of logical tiles, ordered in GROUP_M x GROUP_N blocks
+  // (row-tile groups fastest), so an XCD's concurrent workgroups share both
+  // operands in its L2.
   const int ksplit = (MODE == MODE_GATEUP) ? 1 : p.ksplit;
   const int mgroups = (p.mt_max + GROUP_M - 1) / GROUP_M;
   const int ngroups = (p.nt + GROUP_N - 1) / GROUP_N;
@@ -147,240 +192,110 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   const int64_t G = tiles_per_k * ksplit;
   const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
   const int64_t Lg = (int64_t)(blockIdx.x % NUM_XCD) * chunk + blockIdx.x / NUM_XCD;
-  if (Lg >= G) return;
+  if (Lg >= G) return false;
   const int ks = (int)(Lg / tiles_per_k);
   const int64_t L = Lg % tiles_per_k;
   const int64_t blk = L / (GROUP_M * GROUP_N);
   const int rr = (int)(L % (GROUP_M * GROUP_N));
+  // (uniform values computed with 64-bit VALU arithmetic: pin them to scalar
+  // registers so the buffer resources and offsets built from them need no
+  // per-lane loops)
   const int mslot = __builtin_amdgcn_readfirstlane((int)(blk % mgroups) * GROUP_M + rr % GROUP_M);
   const int ntile = __builtin_amdgcn_readfirstlane((int)(blk / mgroups) * GROUP_N + rr / GROUP_M);
-  if (mslot >= p.mt_max || ntile >= p.nt) return;
+  if (mslot >= p.mt_max || ntile >= p.nt) return false;
 
-  // ---- map the row-tile slot to (expert, first row) from the offsets.
   const int nseg = p.E + (p.has_shared ? 1 : 0);
-  {
-    const int per = (nseg + 255) / 256;
-    const int e_lo = tid * per;
-    int local = 0;
+  const int per = (nseg + 255) / 256;
+  const int e_lo = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e_lo + i;
+    if (e < nseg) {
+      const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
+      local += (int)((rows + BM - 1) / BM);
+    }
+  }
+  const int incl = wave_incl_scan(local, lane);
+  if (lane == 63) s_scan[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w2 = 0; w2 < wave; ++w2) before += s_scan[w2];
+  const int total = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+  int excl = before + incl - local;
+  if (tid == 0 && mslot >= total) s_info[0] = -1;
+  if (mslot >= excl && mslot < excl + local) {
     for (int i = 0; i < per; ++i) {
       const int e = e_lo + i;
-      if (e < nseg) {
-        const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
-        local += (int)((rows + BM - 1) / BM);
+      if (e >= nseg) break;
+      const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
+      const int nt = (int)((rows + BM - 1) / BM);
+      if (mslot < excl + nt) {
+        s_info[0] = e;
+        s_info[1] = (mslot - excl) * BM;
+        s_info[2] = (int)rows;
+        s_info[3] = (e < p.E) ? p.offsets[e] : 0;
+        break;
       }
+      excl += nt;
     }
-    const int incl = wave_incl_scan(local, lane);
-    if (lane == 63) s_scan[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    for (int w2 = 0; w2 < wave; ++w2) before += s_scan[w2];
-    const int total = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
-    int excl = before + incl - local;
-    if (tid == 0 && mslot >= total) s_e = -1;
-    if (mslot >= excl && mslot < excl + local) {
-      for (int i = 0; i < per; ++i) {
-        const int e = e_lo + i;
-        if (e >= nseg) break;
-        const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
-        const int nt = (int)((rows + BM - 1) / BM);
-        if (mslot < excl + nt) {
-          s_e = e;
-          s_m0 = (mslot - excl) * BM;
-          s_rows = (int)rows;
-          s_seg = (e < p.E) ? p.offsets[e] : 0;
-          break;
-        }
-        excl += nt;
-      }
-    }
-    __syncthreads();
   }
-  // The LDS values are the same in every lane; say so to the compiler so the
-  // buffer resources built from them live in scalar registers.
-  const int e = __builtin_amdgcn_readfirstlane(s_e);
-  if (e < 0) return;
-  const int m0 = __builtin_amdgcn_readfirstlane(s_m0);
-  const int rows = __builtin_amdgcn_readfirstlane(s_rows);
-  const int seg = __builtin_amdgcn_readfirstlane(s_seg);
-  const bool shared_e = (e == p.E);
-  const int K = p.K, N = p.N;
-
-  // ---- K range of this workgroup (split-K for the down projection).
-  const int ksteps_all = K / BK;
-  // (uniform values that went through 64-bit VALU arithmetic: pin them to
-  // scalar registers so buffer offsets need no per-lane loops)
-  const int kbeg = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps_all * ks / ksplit));
+  __syncthreads();
+  // The LDS values are the same in every lane.
+  t.e = __builtin_amdgcn_readfirstlane(s_info[0]);
+  if (t.e < 0) return false;
+  t.m0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  t.rows = __builtin_amdgcn_readfirstlane(s_info[2]);
+  t.seg = __builtin_amdgcn_readfirstlane(s_info[3]);
+  t.ntile = ntile;
+  t.shared_e = (t.e == p.E);
+  const int ksteps_all = p.K / BK;
+  t.kbeg = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps_all * ks / ksplit));
   const int kend = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps_all * (ks + 1) / ksplit));
-  const int nk = kend - kbeg;
+  t.nk = kend - t.kbeg;
+  return true;
+}
 
-  // ---- operand sources as buffer loads: one scalar resource per operand
-  // (and per expert matrix), a 32-bit byte offset per thread and row that
-  // stays fixed over K, and the K step in the scalar offset.
-  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
-  const int lr = tid >> 2;         // 0..63: rows lr + 64 i
-  const int kc = (tid & 3) * 8;    // element offset within BK
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)p.A_bytes, kBufferWord3);
-  uint32_t voA[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = min(m0 + lr + 64 * i, rows - 1);
-    int64_t ar;
-    if (MODE == MODE_GATEUP)
-      ar = shared_e ? (int64_t)m : (int64_t)p.perm_token[seg + m];
-    else
-      ar = shared_e ? p.P_max + m : (int64_t)seg + m;
-    voA[i] = (uint32_t)((ar * K + kc) * 2);
-  }
-  // B row r (0..511) of the tile.  GATEUP: rows 0..255 are W1 rows n0 + r,
-  // rows 256..511 are W3 rows n0 + r - 256 (n0 = ntile * 256).  DOWN: W2 rows
-  // n0 + r (n0 = ntile * 512).  Rows past N are clamped (outputs masked).
-  const int n0 = (MODE == MODE_GATEUP) ? ntile * (BNB / 2) : ntile * BNB;
-  const int64_t ebytes = (int64_t)N * K * WB;  // one expert matrix (< 2^31)
-  const char* bptr0 = (const char*)(shared_e ? p.B0s : p.B0) + (shared_e ? 0 : (int64_t)e * ebytes);
-  const __amdgpu_buffer_rsrc_t rsB0 =
-      __builtin_amdgcn_make_buffer_rsrc((void*)bptr0, (short)0, (int)ebytes, kBufferWord3);
-  __amdgpu_buffer_rsrc_t rsB1 = rsB0;
-  if (MODE == MODE_GATEUP) {
-    const char* bptr1 = (const char*)(shared_e ? p.B1s : p.B1) + (shared_e ? 0 : (int64_t)e * ebytes);
-    rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)bptr1, (short)0, (int)ebytes, kBufferWord3);
-  }
-  uint32_t voB[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = lr + 64 * i;
-    int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
-    n = min(n, N - 1);
-    voB[i] = (uint32_t)((n * K + kc) * WB);
-  }
-  // In GATEUP, B loads i = 0..3 come from W1 and i = 4..7 from W3.
+// Row (in elements of K) of activation row m of the tile's segment in the A
+// operand: gathered token rows of x for GATEUP, hidden rows for DOWN*.
+template <int MODE>
+__device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, int m) {
+  if (MODE == MODE_GATEUP) return t.shared_e ? (int64_t)m : (int64_t)p.perm_token[t.seg + m];
+  return t.shared_e ? p.P_max + m : (int64_t)t.seg + m;
+}
 
-  // Three register stages of global loads (A: 2 x 16 B, B: 8 x 16 B per
-  // thread and K step), so a load has two K steps of MFMAs to land.
-  uint4 ra_0[2], rb_0[8], ra_1[2], rb_1[8], ra_2[2], rb_2[8];
-#define MOE_LOAD_STAGE(S, KT)                                                   \
-  do {                                                                          \
-    const int kstep_ = __builtin_amdgcn_readfirstlane(kbeg + (KT));             \
-    ra_##S[0] = buf_load16(rsA, voA[0], kstep_ * BK * 2);                       \
-    ra_##S[1] = buf_load16(rsA, voA[1], kstep_ * BK * 2);                       \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                            \
-      rb_##S[i_] = load_b8<FP8>((MODE == MODE_GATEUP && i_ >= 4) ? rsB1 : rsB0, \
-                                voB[i_], kstep_ * BK * WB);                     \
-  } while (0)
-#define MOE_STORE_STAGE(S, BUF)                                           \
-  do {                                                                    \
-    uint16_t* a_ = As + (BUF) * A_STAGE;                                  \
-    uint16_t* b_ = Bs + (BUF) * B_STAGE;                                  \
-    *(uint4*)&a_[lr * LDSK + kc] = ra_##S[0];                             \
-    *(uint4*)&a_[(lr + 64) * LDSK + kc] = ra_##S[1];                      \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                      \
-      *(uint4*)&b_[(lr + 64 * i_) * LDSK + kc] = rb_##S[i_];              \
-  } while (0)
-
-  // ---- the wave's weight rows: 4 tiles of 32.
-  int brow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (MODE == MODE_GATEUP)
-      brow[j] = (j < 2) ? (wave * 64 + j * 32) : (BNB / 2 + wave * 64 + (j - 2) * 32);
-    else
-      brow[j] = wave * 128 + j * 32;
-  }
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  auto compute = [&](int buf) {
-    const uint16_t* a = As + buf * A_STAGE;
-    const uint16_t* b = Bs + buf * B_STAGE;
-    bf16x8 af[2][4], bfr[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)&a[(i * 32 + frow) * LDSK + fk];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + fk];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) {  // fragments of the next 16 K, read under this step's MFMAs
-        const int ko = (kk + 1) * 16 + fk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[cur ^ 1][i] = *(const bf16x8*)&a[(i * 32 + frow) * LDSK + ko];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[cur ^ 1][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + ko];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (MODE == MODE_GATEUP)  // transposed: acc[i][j] holds [weight row][act row]
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-        }
-    }
-  };
-
-  // ---- main loop, unrolled by the three register stages.  At step kt the
-  // LDS buffer kt & 1 holds step kt, stage (kt + 1) % 3 holds step kt + 1 and
-  // stage (kt + 2) % 3 step kt + 2 (both possibly in flight).  After the
-  // MFMAs, stage kt + 1 goes to the other LDS buffer and stage kt % 3 is
-  // reloaded with step kt + 3.  One barrier per step.
-  if (nk > 0) {
-    MOE_LOAD_STAGE(0, 0);
-    if (nk > 1) MOE_LOAD_STAGE(1, 1);
-    if (nk > 2) MOE_LOAD_STAGE(2, 2);
-    MOE_STORE_STAGE(0, 0);
-    __syncthreads();
-#define MOE_STEP(S0, S1)                                   \
-  {                                                        \
-    const int k_ = kt + (S0);                              \
-    if (k_ >= nk) break;                                   \
-    compute(k_ & 1);                                       \
-    if (k_ + 1 < nk) MOE_STORE_STAGE(S1, (k_ + 1) & 1);    \
-    __syncthreads();                                       \
-    if (k_ + 3 < nk) MOE_LOAD_STAGE(S0, k_ + 3);           \
-  }
-    for (int kt = 0; kt < nk; kt += 3) {
-      MOE_STEP(0, 1)
-      MOE_STEP(1, 2)
-      MOE_STEP(2, 0)
-    }
-#undef MOE_STEP
-  }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
-
-  // ---- epilogue.  32x32 accumulator register r of lane l is row
-  // (r/4)*8 + (l/32)*4 + r%4, column l%32 of the 32x32 tile.
+// Epilogue.  32x32 accumulator register r of lane l is row (r/4)*8 +
+// (l/32)*4 + r%4, column l%32 of the 32x32 tile.  arow0: the wave's first
+// activation row in the tile; brow: its four 32-row weight tiles; n0: first
+// output column of the tile; wn: the wave's column group.
+template <int MODE, bool FP8>
+__device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
+                                           const TileMap& t, int arow0, int n0, int wn,
+                                           const int (&brow)[4]) {
+  const int lane = threadIdx.x & 63;
   const int ccol = lane & 31;
   const int rbase = (lane >> 5) * 4;
+  const int N = p.N;
   if (MODE == MODE_GATEUP) {
-    // acc[i][j]: weight row brow[j] + R, activation row i*32 + ccol.
-    const int64_t hbase = shared_e ? p.P_max : (int64_t)seg;
+    // transposed product: acc[i][j] holds weight row brow[j] + R, activation
+    // row arow0 + i*32 + ccol; tiles j and j + 2 are the gate and up halves.
+    const int64_t hbase = t.shared_e ? p.P_max : (int64_t)t.seg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
-      const int m = m0 + i * 32 + ccol;
-      if (m >= rows) continue;
+      const int m = t.m0 + arow0 + i * 32 + ccol;
+      if (m >= t.rows) continue;
       uint16_t* hrow = p.H + (hbase + m) * N;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wave * 64 + j * 32 + q * 8 + rbase;  // 4 consecutive columns
+          const int n = n0 + wn * 64 + j * 32 + q * 8 + rbase;  // 4 consecutive columns
           if (n >= N) continue;
           float sg = 1.f, su = 1.f;
           if (FP8) {
             const int gi = n / kFp8Group;
-            sg = shared_e ? p.sc0s[gi] : p.sc0[(int64_t)e * (N / kFp8Group) + gi];
-            su = shared_e ? p.sc1s[gi] : p.sc1[(int64_t)e * (N / kFp8Group) + gi];
+            sg = t.shared_e ? p.sc0s[gi] : p.sc0[(int64_t)t.e * (N / kFp8Group) + gi];
+            su = t.shared_e ? p.sc1s[gi] : p.sc1[(int64_t)t.e * (N / kFp8Group) + gi];
           }
           uint32_t hb[4];
 #pragma unroll
@@ -397,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
       }
     }
   } else {
-    // acc[i][j]: activation row i*32 + R, weight row (output column) brow[j] + ccol.
+    // acc[i][j]: activation row arow0 + i*32 + R, output column brow[j] + ccol.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -405,19 +320,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = m0 + i * 32 + q * 8 + rbase + r;
-          if (m >= rows) continue;
+          const int m = t.m0 + arow0 + i * 32 + q * 8 + rbase + r;
+          if (m >= t.rows) continue;
           float wgt = 1.f;
           int64_t orow;
           if (MODE == MODE_DOWN) {
-            if (shared_e) {
+            if (t.shared_e) {
               orow = m;
             } else {
-              orow = p.perm_token[seg + m];
-              wgt = p.perm_w[seg + m];
+              orow = p.perm_token[t.seg + m];
+              wgt = p.perm_w[t.seg + m];
             }
           } else {
-            orow = (int64_t)seg + m;
+            orow = (int64_t)t.seg + m;
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -426,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
             float v = acc[i][j][q * 4 + r];
             if (FP8) {
               const int gi = n / kFp8Group;
-              v *= shared_e ? p.sc0s[gi] : p.sc0[(int64_t)e * (N / kFp8Group) + gi];
+              v *= t.shared_e ? p.sc0s[gi] : p.sc0[(int64_t)t.e * (N / kFp8Group) + gi];
             }
             if (MODE == MODE_DOWN)
               atomicAdd(&p.y[orow * N + n], wgt * v);
@@ -439,6 +354,356 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   }
 }
 
+// The wave's four 32-row weight tiles.  GATEUP: 64 gate rows then the same
+// 64 up rows (which sit BNB/2 further in the tile); DOWN*: 128 rows.
+template <int MODE, int BNB>
+__device__ __forceinline__ void wave_brows(int wn, int (&brow)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (MODE == MODE_GATEUP)
+      brow[j] = (j < 2) ? (wn * 64 + j * 32) : (BNB / 2 + wn * 64 + (j - 2) * 32);
+    else
+      brow[j] = wn * 128 + j * 32;
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// 16 MFMAs of one 16-deep K slice.  GATEUP computes the transposed product
+// (weights as the A operand) so lanes hold consecutive hidden columns.
+template <int MODE>
+__device__ __forceinline__ void mfma_slice(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
+                                           const bf16x8 (&bfr)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (MODE == MODE_GATEUP)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel (used for fp8 weights, which are widened to bf16 on
+// their way into LDS, and as the fallback of the LDS-DMA kernel).
+template <int MODE, bool FP8, int BM>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
+  using TL = Tile<BM>;
+  constexpr int BNB = TL::BNB, NA = TL::NA, NB = TL::NB;
+  constexpr int A_STAGE = TL::A_STAGE, B_STAGE = TL::B_STAGE;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* As = lds;                    // [2][BM][LDSK]
+  uint16_t* Bs = lds + 2 * A_STAGE;      // [2][BNB][LDSK]
+
+  TileMap t;
+  if (!map_tile<MODE, BM>(p, t)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int K = p.K, N = p.N, kbeg = t.kbeg, nk = t.nk;
+
+  // ---- operand sources as buffer loads: one scalar resource per operand
+  // (and per expert matrix), a 32-bit byte offset per thread and row that
+  // stays fixed over K, and the K step in the scalar offset.
+  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
+  const int lr = tid >> 2;         // 0..63: rows lr + 64 i
+  const int kc = (tid & 3) * 8;    // element offset within BK
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)p.A_bytes, kBufferWord3);
+  uint32_t voA[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int m = min(t.m0 + lr + 64 * i, t.rows - 1);
+    voA[i] = (uint32_t)((a_row<MODE>(p, t, m) * K + kc) * 2);
+  }
+  // B row r of the tile.  GATEUP: rows < BNB/2 are W1 rows n0 + r, the rest
+  // W3 rows n0 + r - BNB/2 (n0 = ntile * BNB/2).  DOWN: W2 rows n0 + r
+  // (n0 = ntile * BNB).  Rows past N are clamped (outputs masked).
+  const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
+  const int64_t ebytes = (int64_t)N * K * WB;  // one expert matrix (< 2^31)
+  const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
+  const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)(t.shared_e ? p.B0s : p.B0) + eoff), (short)0, (int)ebytes, kBufferWord3);
+  __amdgpu_buffer_rsrc_t rsB1 = rsB0;
+  if (MODE == MODE_GATEUP)
+    rsB1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)(t.shared_e ? p.B1s : p.B1) + eoff), (short)0, (int)ebytes, kBufferWord3);
+  uint32_t voB[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r = lr + 64 * i;
+    int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+    n = min(n, N - 1);
+    voB[i] = (uint32_t)((n * K + kc) * WB);
+  }
+  // In GATEUP, B loads i < NB/2 come from W1 and the rest from W3.
+
+  // Three register stages of global loads, so a load has two K steps of MFMAs
+  // to land.  (static_for, not a pragma-unrolled loop: this compiler
+  // otherwise keeps the stage arrays in scratch memory.)
+  uint4 ra_0[NA], rb_0[NB], ra_1[NA], rb_1[NB], ra_2[NA], rb_2[NB];
+#define MOE_LOAD_STAGE(S, KT)                                                           \
+  do {                                                                                  \
+    const int kstep_ = __builtin_amdgcn_readfirstlane(kbeg + (KT));                     \
+    static_for<NA>([&](auto i_) { ra_##S[i_] = buf_load16(rsA, voA[i_], kstep_ * BK * 2); }); \
+    static_for<NB>([&](auto i_) {                                                       \
+      rb_##S[i_] = load_b8<FP8>((MODE == MODE_GATEUP && i_ >= NB / 2) ? rsB1 : rsB0,    \
+                                voB[i_], kstep_ * BK * WB);                             \
+    });                                                                                 \
+  } while (0)
+#define MOE_STORE_STAGE(S, BUF)                                                         \
+  do {                                                                                  \
+    uint16_t* a_ = As + (BUF) * A_STAGE;                                                \
+    uint16_t* b_ = Bs + (BUF) * B_STAGE;                                                \
+    static_for<NA>([&](auto i_) { *(uint4*)&a_[(lr + 64 * i_) * LDSK + kc] = ra_##S[i_]; }); \
+    static_for<NB>([&](auto i_) { *(uint4*)&b_[(lr + 64 * i_) * LDSK + kc] = rb_##S[i_]; }); \
+  } while (0)
+
+  // ---- the wave's 128 activation rows and 128 weight rows (4 tiles of 32).
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int arow0 = wm * 128;
+  int brow[4];
+  wave_brows<MODE, BNB>(wn, brow);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+    const uint16_t* a = As + buf * A_STAGE;
+    const uint16_t* b = Bs + buf * B_STAGE;
+    bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)&a[(arow0 + i * 32 + frow) * LDSK + fk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + fk];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {  // fragments of the next 16 K, read under this step's MFMAs
+        const int ko = (kk + 1) * 16 + fk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[cur ^ 1][i] = *(const bf16x8*)&a[(arow0 + i * 32 + frow) * LDSK + ko];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[cur ^ 1][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + ko];
+      }
+      mfma_slice<MODE>(acc, af[cur], bfr[cur]);
+    }
+  };
+
+  // ---- main loop, unrolled by the three register stages.  At the top of an
+  // iteration LDS buffer kt & 1 holds step kt, stage 1 holds step kt + 1 and
+  // stage 2 step kt + 2 (possibly still in flight); stage 0 is free.  Each
+  // sub-step computes one K step, moves the next stage into the other LDS
+  // buffer and reloads the stage it freed three steps ahead.  The loop has a
+  // single exit (no early breaks: those make the accumulators merge at several
+  // points, which this compiler answers with register copies); the 0..2
+  // leftover steps follow in straight-line code.  One barrier per step.
+  if (nk > 0) {
+    MOE_LOAD_STAGE(0, 0);
+    if (nk > 1) MOE_LOAD_STAGE(1, 1);
+    if (nk > 2) MOE_LOAD_STAGE(2, 2);
+    MOE_STORE_STAGE(0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+      compute(kt & 1);
+      MOE_STORE_STAGE(1, (kt + 1) & 1);
+      __syncthreads();
+      if (kt + 3 < nk) MOE_LOAD_STAGE(0, kt + 3);
+      compute((kt + 1) & 1);
+      MOE_STORE_STAGE(2, kt & 1);
+      __syncthreads();
+      if (kt + 4 < nk) MOE_LOAD_STAGE(1, kt + 4);
+      compute(kt & 1);
+      if (kt + 3 < nk) MOE_STORE_STAGE(0, (kt + 1) & 1);
+      __syncthreads();
+      if (kt + 5 < nk) MOE_LOAD_STAGE(2, kt + 5);
+    }
+    const int rem = nk - kt;
+    if (rem >= 1) {
+      compute(kt & 1);
+      if (rem >= 2) {
+        MOE_STORE_STAGE(1, (kt + 1) & 1);
+        __syncthreads();
+        compute((kt + 1) & 1);
+      }
+    }
+  }
+#undef MOE_LOAD_STAGE
+#undef MOE_STORE_STAGE
+  store_tile<MODE, FP8>(p, acc, t, arow0, n0, wn, brow);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-DMA kernel for bf16 weights: 256 x 256 tiles (2 x 2 waves of 128 x 128),
+// operands moved global -> LDS by buffer_load ... lds (no register staging,
+// no LDS write instructions), NS stage buffers of KB-deep K steps, filled
+// NS - 1 steps ahead.  Rows are KB*2 bytes; their 16-byte chunks are
+// XOR-swizzled by (row / rows-per-256-bytes) % chunks-per-row, so the 16-byte
+// fragment reads of 32 consecutive rows hit distinct banks while each
+// wave-level DMA instruction still writes 1 KiB contiguously.
+constexpr int DMA_BM = 256;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int KB, int NS>
+struct DmaCfg {
+  static constexpr int RB = KB * 2;                 // bytes per tile row and stage
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int RPS = 256 / RB;              // rows per 256-byte bank sweep
+  static constexpr int ROWS_PER_INST = 1024 / RB;   // rows one wave-level DMA fills
+  static constexpr int NI = 512 / ROWS_PER_INST / 4;  // DMA instructions per wave and stage
+  static constexpr int TILE_BYTES = 256 * RB;       // one operand tile (A or B)
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
+  static_assert(KB % 16 == 0 && NS >= 2 && NS <= 4, "DMA pipeline shape");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int MODE, int KB, int NS, int MOE_AUX>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  using C = DmaCfg<KB, NS>;
+  constexpr int BNB = 256;
+  extern __shared__ __attribute__((aligned(1024))) char dlds[];
+  TileMap t;
+  if (!map_tile<MODE, DMA_BM>(p, t)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = p.K, N = p.N;
+  // K steps of KB (the workgroup's K range is given in steps of BK)
+  const int kbeg_el = t.kbeg * BK;
+  const int nk = (t.nk * BK) / KB;
+
+  // ---- DMA sources.  Waves 0, 1 fill the A tile, waves 2, 3 the B tile
+  // (in GATEUP wave 2 the W1 rows, wave 3 the W3 rows).  Wave w's instruction
+  // j fills tile rows ((w & 1) * NI + j) * ROWS_PER_INST + lane / CPR; lane
+  // i writes chunk slot i % CPR, which holds K chunk (i % CPR) ^ swz(row).
+  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A, p.A_bytes);
+  const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
+  const int64_t ebytes = (int64_t)N * K * 2;
+  const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
+  const __amdgpu_buffer_rsrc_t rsB0 =
+      uniform_rsrc((const char*)(t.shared_e ? p.B0s : p.B0) + eoff, ebytes);
+  __amdgpu_buffer_rsrc_t rsB1 = rsB0;
+  if (MODE == MODE_GATEUP)
+    rsB1 = uniform_rsrc((const char*)(t.shared_e ? p.B1s : p.B1) + eoff, ebytes);
+  uint32_t voff[C::NI];
+  static_for<C::NI>([&](auto j) {
+    const int r = ((wave & 1) * C::NI + j) * C::ROWS_PER_INST + lane / C::CPR;  // 0..255
+    const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
+    if (wave < 2) {
+      const int m = min(t.m0 + r, t.rows - 1);
+      voff[j] = (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16);
+    } else {
+      int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+      n = min(n, N - 1);
+      voff[j] = (uint32_t)(((int64_t)n * K + kbeg_el) * 2 + chunk * 16);
+    }
+  });
+  // Branching on the (scalar) wave index keeps each resource in scalar registers.
+  // With krot, workgroup tiles start their K walk at different points, so
+  // concurrent workgroups do not all read the same K slice (row strides are
+  // K*2 bytes, a power of two in the common shapes).
+  const int krot = p.krot ? __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)max(nk, 1))) : 0;
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    char* gbase = dlds + stage * C::STAGE_BYTES + (wave >> 1) * C::TILE_BYTES +
+                  (wave & 1) * (C::TILE_BYTES / 2);
+    int kr = kt + krot;
+    kr = kr >= nk ? kr - nk : kr;
+    const int soff = __builtin_amdgcn_readfirstlane(kr * C::RB);
+    if (wave < 2) {
+      static_for<C::NI>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+      });
+    } else if (MODE == MODE_GATEUP && wave == 3) {
+      static_for<C::NI>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+      });
+    } else {
+      static_for<C::NI>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+      });
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int arow0 = wm * 128;
+  int brow[4];
+  wave_brows<MODE, BNB>(wn, brow);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+
+  // fragment reads: tile rows are 32-aligned, so swz(row) = (frow / RPS) % CPR
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+  const int swz = (frow / C::RPS) % C::CPR;
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const char* a = dlds + stage * C::STAGE_BYTES;
+    const char* b = a + C::TILE_BYTES;
+    // one 32-deep half at a time: 16 fragment reads in flight, then 32 MFMAs
+    static_for<KB / 32>([&](auto h) {
+      bf16x8 af[2][4], bfr[2][4];
+      static_for<2>([&](auto kk) {
+        const int c = (h * 4 + kk * 2 + fhalf) ^ swz;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[kk][i] = *(const bf16x8*)(a + (arow0 + i * 32 + frow) * C::RB + c * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfr[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + c * 16);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_slice<MODE>(acc, af[0], bfr[0]);
+      mfma_slice<MODE>(acc, af[1], bfr[1]);
+    });
+  };
+
+  // ---- pipeline.  Before computing step kt a wave waits until its own DMA
+  // for step kt has landed (the DMA of the following steps already issued
+  // may still be in flight), then a barrier makes every wave's part visible
+  // and frees the stage computed at kt - 1, which is refilled with step
+  // kt + NS - 1.  (A bare s_barrier: the fence of __syncthreads would wait
+  // for all DMA.)
+  if (nk > 0) {
+    static_for<NS - 1>([&](auto s) {
+      if (s < nk) issue(s, s);
+    });
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(nk - 1 - kt, NS - 2);  // later steps already issued
+      if (ahead >= 2)
+        wait_vmcnt<2 * C::NI>();
+      else if (ahead == 1)
+        wait_vmcnt<C::NI>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
+      compute(kt % NS);
+    }
+  }
+  store_tile<MODE, false>(p, acc, t, arow0, n0, wn, brow);
+}
+
+// Linear+bias experts in fp32 (the tutorial's nn.Linear(d, d) experts, §4.1).
+// One thread per (grouped row, output feature); MODE_DOWN adds w * out into y.
 template <int MODE>
 __global__ __launch_bounds__(256) void linear_bias_kernel(
     const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ b,
@@ -487,9 +752,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-constexpr size_t kGemmLds = (size_t)2 * (A_STAGE + B_STAGE) * sizeof(uint16_t);
-
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, int BM>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
   const int64_t mg = (p.mt_max + GROUP_M - 1) / GROUP_M;
@@ -497,15 +760,74 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
   const int64_t G = mg * ng * GROUP_M * GROUP_N * (MODE == MODE_GATEUP ? 1 : p.ksplit);
   static bool attr_set = false;  // opt in to more than 64 KiB of LDS, once per process
   if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, FP8>,
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, FP8, BM>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)kGemmLds);
+                                         (int)Tile<BM>::LDS);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
   const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
-  grouped_gemm_kernel<MODE, FP8><<<(unsigned)(chunk * NUM_XCD), 256, kGemmLds, st>>>(p);
+  grouped_gemm_kernel<MODE, FP8, BM><<<(unsigned)(chunk * NUM_XCD), 256, Tile<BM>::LDS, st>>>(p);
   return hipGetLastError();
+}
+
+template <int MODE, int KB, int NS, int AUX = 0>
+hipError_t launch_gemm_dma_cfg(const GemmParams& p, hipStream_t st) {
+  const int64_t mg = (p.mt_max + GROUP_M - 1) / GROUP_M;
+  const int64_t ng = (p.nt + GROUP_N - 1) / GROUP_N;
+  const int64_t G = mg * ng * GROUP_M * GROUP_N * (MODE == MODE_GATEUP ? 1 : p.ksplit);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, KB, NS, AUX>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)DmaCfg<KB, NS>::LDS);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
+  grouped_gemm_dma_kernel<MODE, KB, NS, AUX>
+      <<<(unsigned)(chunk * NUM_XCD), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
+  return hipGetLastError();
+}
+
+// DMA pipeline shape: K per stage x stages (MOE_GEMM_DMA_CFG=32x4|32x3|64x2
+// for tuning).  A K range that is not a multiple of 64 takes 32-deep steps.
+template <int MODE>
+hipError_t launch_gemm_dma(const GemmParams& p, hipStream_t st) {
+  if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
+  const char* v = getenv("MOE_GEMM_DMA_CFG");
+  const int ksteps = p.K / BK;  // whole-K steps of 32
+  const bool k64_ok = (ksteps % (2 * (MODE == MODE_GATEUP ? 1 : p.ksplit)) == 0);
+  if (v && !strcmp(v, "32x3")) return launch_gemm_dma_cfg<MODE, 32, 3>(p, st);
+  if (v && !strcmp(v, "32x4")) return launch_gemm_dma_cfg<MODE, 32, 4>(p, st);
+  if (k64_ok) {
+    if (p.cache_aux == 1) return launch_gemm_dma_cfg<MODE, 64, 2, 1>(p, st);
+    if (p.cache_aux == 2) return launch_gemm_dma_cfg<MODE, 64, 2, 2>(p, st);
+    return launch_gemm_dma_cfg<MODE, 64, 2>(p, st);
+  }
+  return launch_gemm_dma_cfg<MODE, 32, 4>(p, st);
+}
+
+// bf16 weights with 256-row tiles take the LDS-DMA kernel unless
+// MOE_GEMM_DMA=0; fp8 weights the register-staged one.
+template <int MODE, int BM>
+hipError_t launch_gemm_dt(const GemmParams& p, bool fp8, hipStream_t st) {
+  if (fp8) return launch_gemm<MODE, true, BM>(p, st);
+  const char* v = getenv("MOE_GEMM_DMA");
+  if (BM == DMA_BM && !(v && atoi(v) == 0)) return launch_gemm_dma<MODE>(p, st);
+  return launch_gemm<MODE, false, BM>(p, st);
+}
+
+// Row-tile height of the grouped GEMMs: 256 (256 x 256 tiles; LDS-DMA kernel
+// for bf16 weights) by default, or 128 (128 x 512 tiles, register-staged);
+// MOE_GEMM_BM, MOE_GEMM_BM_GATEUP and MOE_GEMM_BM_DOWN override it (tuning).
+int gemm_bm(int mode, int64_t rows_per_expert) {
+  const char* v = getenv(mode == MODE_GATEUP ? "MOE_GEMM_BM_GATEUP" : "MOE_GEMM_BM_DOWN");
+  if (!v) v = getenv("MOE_GEMM_BM");
+  if (v) return atoi(v) == 128 ? 128 : 256;
+  // few rows per expert (decode): 128-row tiles waste half as many MFMAs on
+  // padding rows, and the weights, not the MFMAs, set the time
+  return rows_per_expert < 128 ? 128 : 256;
 }
 
 }  // namespace
@@ -533,7 +855,11 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   const bool fp8 = s.w_dtype == MOE_DT_FP8_E4M3;
   const int has_sh = s.has_shared ? 1 : 0;
   // Upper bound of row tiles: sum_e ceil(rows_e / BM) <= P_max / BM + E (+ shared).
-  const int64_t mt_max = (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
+  auto mt_bound = [&](int BM) {
+    return (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
+  };
+  const int64_t rows_per_expert = L.P_max / std::max(1, s.E);
+  const int bm1 = gemm_bm(MODE_GATEUP, rows_per_expert), bm2 = gemm_bm(MODE_DOWN, rows_per_expert);
 
   GemmParams g{};
   g.perm_token = perm_token;
@@ -543,8 +869,14 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.P_max = L.P_max;
   g.E = s.E;
   g.has_shared = has_sh;
-  g.mt_max = (int)mt_max;
+  g.mt_max = (int)mt_bound(bm1);
   g.ksplit = 1;
+  {
+    const char* kr = getenv("MOE_GEMM_KROT");
+    const char* ax = getenv("MOE_GEMM_AUX");
+    g.krot = kr ? atoi(kr) : 0;
+    g.cache_aux = ax ? atoi(ax) : 1;
+  }
 
   // gate / up
   g.A = (const uint16_t*)x;
@@ -554,9 +886,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.H = (uint16_t*)H;
   g.K = s.d;
   g.N = s.d_ff;
-  g.nt = (s.d_ff + BNB / 2 - 1) / (BNB / 2);
-  hipError_t err = fp8 ? launch_gemm<MODE_GATEUP, true>(g, st)
-                       : launch_gemm<MODE_GATEUP, false>(g, st);
+  const int bn1 = 65536 / bm1 / 2;  // hidden columns per gate/up tile
+  g.nt = (s.d_ff + bn1 - 1) / bn1;
+  hipError_t err = bm1 == 256 ? launch_gemm_dt<MODE_GATEUP, 256>(g, fp8, st)
+                              : launch_gemm_dt<MODE_GATEUP, 128>(g, fp8, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {
     err = hipEventRecord(ev_mid, st);
@@ -574,20 +907,26 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.y_perm = y_perm;
   g2.K = s.d_ff;
   g2.N = s.d;
-  g2.nt = (s.d + BNB - 1) / BNB;
-  // Split K when the tile grid would leave CUs idle (decode-sized T); only
-  // with the atomic combine, whose adds also take the partial sums.
+  const int bn2 = 65536 / bm2;  // output columns per down tile
+  g2.nt = (s.d + bn2 - 1) / bn2;
+  g2.mt_max = (int)mt_bound(bm2);
+  // Split K only when the tile grid is small (decode-sized T), so that every
+  // CU streams weights; only with the atomic combine, whose adds also take the
+  // partial sums.  (On large grids the extra atomic passes into y cost more
+  // than the fuller last round of tiles gains.)
   if (y) {
-    const int64_t tiles = (int64_t)(L.P_max / BM + std::min<int64_t>(s.E, L.P_max) + has_sh) * g2.nt;
-    const int ksteps = s.d_ff / BK;
+    const int64_t est_rows_tiles = L.P_max / bm2 + (s.E + 1) / 2 + (has_sh ? (s.T + bm2 - 1) / bm2 : 0);
+    const int64_t tiles = std::max<int64_t>(1, std::min<int64_t>(est_rows_tiles, g2.mt_max)) * g2.nt;
+    const int ks_max = std::max(1, s.d_ff / BK / 8);
     int ks = 1;
-    while (tiles * ks < 512 && ks * 2 <= ksteps / 8) ks *= 2;
+    while (tiles * ks < 512 && ks * 2 <= ks_max) ks *= 2;
     g2.ksplit = ks;
   }
   if (y)
-    return fp8 ? launch_gemm<MODE_DOWN, true>(g2, st) : launch_gemm<MODE_DOWN, false>(g2, st);
-  return fp8 ? launch_gemm<MODE_DOWN_PERM, true>(g2, st)
-             : launch_gemm<MODE_DOWN_PERM, false>(g2, st);
+    return bm2 == 256 ? launch_gemm_dt<MODE_DOWN, 256>(g2, fp8, st)
+                      : launch_gemm_dt<MODE_DOWN, 128>(g2, fp8, st);
+  return bm2 == 256 ? launch_gemm_dt<MODE_DOWN_PERM, 256>(g2, fp8, st)
+                    : launch_gemm_dt<MODE_DOWN_PERM, 128>(g2, fp8, st);
 }
 
 hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* slot_pos,

@@ -87,13 +87,6 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 4) {
     if (_st != MOE_OK) return _st;  \
   } while (0)
 
-int router_splits(const moe_shape& s) {
-  const int64_t mt = (s.T + 63) / 64;
-  const int kmax = std::max(1, (s.d + 63) / 64);
-  int sp = (int)std::min<int64_t>(kmax, std::max<int64_t>(1, (512 + mt - 1) / std::max<int64_t>(mt, 1)));
-  return std::max(1, sp);
-}
-
 moe_status check_weights(const moe_shape* s, const moe_weights* w) {
   if (!w) return fail(MOE_ERR_INVALID, "weights is NULL");
   if (s->kind == MOE_EXPERT_LINEAR_BIAS) {
@@ -126,6 +119,7 @@ moe_status check_weights(const moe_shape* s, const moe_weights* w) {
 
 struct Ws {
   float* partial;
+  void* wsplit;
   int32_t* chunk_hist;
   int32_t* chunk_base;
   int32_t* perm_token;
@@ -136,7 +130,7 @@ struct Ws {
 
 Ws carve(const WsLayout& L, void* ws) {
   char* b = (char*)ws;
-  return Ws{(float*)(b + L.off_partial),     (int32_t*)(b + L.off_chunk_hist),
+  return Ws{(float*)(b + L.off_partial),     (void*)(b + L.off_wsplit), (int32_t*)(b + L.off_chunk_hist),
             (int32_t*)(b + L.off_chunk_base), (int32_t*)(b + L.off_perm_token),
             (float*)(b + L.off_perm_w),       (int32_t*)(b + L.off_slot_pos),
             (void*)(b + L.off_H)};
@@ -184,13 +178,15 @@ struct CallEvents {
 WsLayout ws_layout(const moe_shape& s) {
   WsLayout L{};
   const int64_t A = s.T * (int64_t)s.top_k;
-  L.router_splits = router_splits(s);
+  L.router_splits = router_splits_for(s);
   L.nchunks = (int)std::max<int64_t>(1, (A + kDispatchChunk - 1) / kDispatchChunk);
   L.P_max = (s.capacity < 0) ? A : std::min<int64_t>(A, (int64_t)s.E * s.capacity);
   L.H_rows = L.P_max + (s.has_shared ? s.T : 0);
   size_t off = 0;
   L.off_partial = off;
   off = align256(off + (size_t)L.router_splits * s.T * s.E * sizeof(float));
+  L.off_wsplit = off;
+  off = align256(off + router_split_bytes(s));
   L.off_chunk_hist = off;
   off = align256(off + (size_t)L.nchunks * s.E * sizeof(int32_t));
   L.off_chunk_base = off;
@@ -240,7 +236,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* W_g, co
   const WsLayout L = ws_layout(s);
   const Ws W = carve(L, ws);
   hipStream_t st = (hipStream_t)stream;
-  MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, st), "router gemm"));
+  MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, W.wsplit, st), "router gemm"));
   return hip_status(launch_topk(s, W.partial, L.router_splits, b_g, logits, topk_idx, topk_w, st),
                     "top-k");
 }
@@ -358,7 +354,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   MOE_TRY(check_weights(&s, w));
   CallEvents ce;
   ce.begin(st);
-  MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, st), "router gemm"));
+  MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, W.wsplit, st), "router gemm"));
   ce.mark(1, st);
   MOE_TRY(hip_status(launch_topk(s, W.partial, L.router_splits, b_g, nullptr, topk_idx, topk_w, st),
                      "top-k"));

@@ -33,6 +33,7 @@ struct WsLayout {
   int64_t P_max;         // upper bound of kept assignments
   int64_t H_rows;        // rows of the hidden buffer (P_max + T for a shared expert)
   size_t off_partial;    // fp32 [router_splits, T, E]
+  size_t off_wsplit;     // bf16 [3, E_pad, d] split router weights (MFMA router)
   size_t off_chunk_hist; // int32 [nchunks, E]
   size_t off_chunk_base; // int32 [nchunks, E]
   size_t off_perm_token; // int32 [P_max]
@@ -46,8 +47,10 @@ WsLayout ws_layout(const moe_shape& s);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All are asynchronous.
+int router_splits_for(const moe_shape& s);
+size_t router_split_bytes(const moe_shape& s);
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
-                              float* partial, int splits, hipStream_t st);
+                              float* partial, int splits, void* split_ws, hipStream_t st);
 hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
                        const float* b_g, float* logits, int32_t* topk_idx,
                        float* topk_w, hipStream_t st);

@@ -6,10 +6,13 @@
 // renormalisation).  Both formulations give the same weights; the selection is
 // made on the logits (softmax is monotone), ties to the lower expert index.
 //
-// Stage A (router_gemm_kernel): split-K partial dot products written to
-// partial[split][t][e].  One workgroup = 64 tokens x all experts x one K
-// range; lane = token, each wave owns a contiguous group of experts whose
-// weights it reads with wave-uniform (scalar) loads.
+// Stage A: split-K partial dot products written to partial[split][t][e].
+//   bf16 activations (router_split_kernel + router_mfma_kernel): the fp32
+//   gate is split exactly into three bf16 parts and contracted on bf16 MFMA
+//   with fp32 accumulation (fp32-GEMM accuracy at matrix-core speed).
+//   fp32 activations (router_gemm_kernel): one workgroup = 64 tokens x all
+//   experts x one K range; lane = token, each wave owns a contiguous group of
+//   experts whose weights it reads with wave-uniform (scalar) loads.
 // Stage B (topk_kernel): L lanes per token (L = min(64, pow2 >= E)) sum the
 // partials in a fixed order (deterministic), add the bias, and run k rounds of
 // a lane-group arg-max on a 64-bit key (ordered logit bits, then ~expert).
@@ -74,6 +77,90 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
     for (int i = 0; i < EPW; ++i)
       if (e0 + i < E) out[i] = acc[i];
   }
+}
+
+// ---- MFMA router for bf16 activations.
+// The fp32 gate weights are split exactly into three bf16 parts,
+// W = hi + mid + lo (each part takes the next 8 significand bits; the
+// remainders are exact in fp32), stored transposed [3][E_pad][d].  Each
+// product of a bf16 activation with a bf16 part is exact in fp32, and the
+// MFMA accumulates in fp32, so the logits carry fp32-GEMM accuracy.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W_g, int d,
+                                                           int E, int E_pad,
+                                                           uint16_t* __restrict__ Wp) {
+  const int64_t n = (int64_t)E_pad * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int e = (int)(i / d);
+    const int k = (int)(i % d);
+    const float w = (e < E) ? W_g[(int64_t)k * E + e] : 0.f;
+    const uint32_t h = f32_to_bf16_bits(w);
+    const float r1 = w - bf16_bits_to_f32(h);
+    const uint32_t m = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(m);
+    const uint32_t l = f32_to_bf16_bits(r2);
+    Wp[i] = (uint16_t)h;
+    Wp[n + i] = (uint16_t)m;
+    Wp[2 * n + i] = (uint16_t)l;
+  }
+}
+
+// One wave: 64 token rows x 16*NJ experts (16x16x32 MFMA tiles); a workgroup
+// of 4 waves covers 256 rows.  Operand fragments (16 bytes per lane: row
+// lane%16, K chunk lane/16) are read straight from global memory; the
+// workgroup's K range is one split of the reduction.
+template <int NJ>
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ Wp,
+                                                          float* __restrict__ partial, int64_t T,
+                                                          int d, int E, int E_pad, int ksteps_per) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  const int split = blockIdx.y;
+  const int k0 = split * ksteps_per * 32;
+  const int k1 = min(d, k0 + ksteps_per * 32);
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = min(r0 + i * 16 + fr, T - 1);
+    arow[i] = x + t * d + fk;
+  }
+  const int64_t plane = (int64_t)E_pad * d;
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = k0; k < k1; k += 32) {
+    bf16x8_t a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(arow[i] + k);
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8_t b = *(const bf16x8_t*)(Wp + part * plane + (int64_t)(j * 16 + fr) * d + k + fk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert j*16 + lane%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = r0 + i * 16 + (lane >> 4) * 4 + r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = j * 16 + fr;
+        if (e < E) partial[((int64_t)split * T + t) * E + e] = acc[i][j][r];
+      }
+    }
 }
 
 // Ordered key: larger logit -> larger key; equal logits -> lower expert larger.
@@ -172,8 +259,52 @@ hipError_t router_gemm_dispatch(const moe_shape& s, const XT* x, const float* W_
 
 }  // namespace
 
+int router_mfma_epad(const moe_shape& s) {
+  if (s.act_dtype != MOE_DT_BF16 || s.d % 32 != 0 || s.E > 256) return 0;
+  int e = 16;
+  while (e < s.E) e *= 2;
+  return e;
+}
+
+size_t router_split_bytes(const moe_shape& s) {
+  const int ep = router_mfma_epad(s);
+  return ep ? (size_t)3 * ep * s.d * sizeof(uint16_t) : 0;
+}
+
+int router_splits_for(const moe_shape& s) {
+  if (router_mfma_epad(s)) {
+    const int64_t wgs = (s.T + 255) / 256;
+    const int ksteps = s.d / 32;
+    int sp = 1;
+    while (wgs * sp < 256 && ksteps / (sp * 2) >= 4) sp *= 2;
+    return sp;
+  }
+  const int64_t mt = (s.T + 63) / 64;
+  const int kmax = std::max(1, (s.d + 63) / 64);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kmax, (512 + mt - 1) / std::max<int64_t>(mt, 1)));
+}
+
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
-                              float* partial, int splits, hipStream_t st) {
+                              float* partial, int splits, void* split_ws, hipStream_t st) {
+  const int ep = router_mfma_epad(s);
+  if (ep) {
+    uint16_t* Wp = (uint16_t*)split_ws;
+    const int64_t n = (int64_t)ep * s.d;
+    router_split_kernel<<<(unsigned)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, st>>>(
+        W_g, s.d, s.E, ep, Wp);
+    const int ksteps = s.d / 32;
+    const int per = (ksteps + splits - 1) / splits;
+    dim3 grid((unsigned)((s.T + 255) / 256), (unsigned)splits);
+#define MOE_RM(NJ)                                                                           \
+  if (ep == NJ * 16) {                                                                       \
+    router_mfma_kernel<NJ><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d, \
+                                                 s.E, ep, per);                              \
+    return hipGetLastError();                                                                \
+  }
+    MOE_RM(1) MOE_RM(2) MOE_RM(4) MOE_RM(8) MOE_RM(16)
+#undef MOE_RM
+    return hipErrorInvalidValue;
+  }
   if (s.act_dtype == MOE_DT_F32)
     return router_gemm_dispatch<float>(s, (const float*)x, W_g, partial, splits, st);
   return router_gemm_dispatch<uint16_t>(s, (const uint16_t*)x, W_g, partial, splits, st);

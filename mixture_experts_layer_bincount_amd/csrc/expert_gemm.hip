@@ -26,17 +26,18 @@
 // reads) fed from three register stages, so each global load has two K steps
 // of MFMAs to land; fragments of the next 16 K are read from LDS under the
 // current MFMAs; one barrier per K step.
-// Tile order: a 1-D grid remapped so that the workgroups one XCD runs at the
-// same time cover an 8 (row tiles) x 4 (weight tiles) block, sharing both
-// operands in that XCD's L2.  The down projection may split K across
-// workgroups when the tile grid is small (decode); partial sums are added
-// by the same atomics.
+// Tile order (tile_sched.h): the real tiles, counted on the device, are dealt
+// evenly to the XCDs in 8 (row tiles) x 4 (weight tiles) blocks, so the
+// workgroups one XCD runs at the same time share both operands in its L2;
+// with the atomic combine the tiles of the last, partial round are split over
+// K and their partial sums added by the same atomics.
 #include <stdlib.h>
 #include <string.h>
 
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "tile_sched.h"
 
 namespace moe {
 namespace {
@@ -61,9 +62,6 @@ struct Tile {
   static constexpr int B_STAGE = BNB * LDSK;
   static constexpr size_t LDS = (size_t)2 * (A_STAGE + B_STAGE) * sizeof(uint16_t);
 };
-constexpr int GROUP_M = 8;    // row tiles per XCD block
-constexpr int GROUP_N = 4;    // weight tiles per XCD block
-constexpr int NUM_XCD = 8;
 
 struct GemmParams {
   const uint16_t* A;          // GATEUP: x [T, K]; DOWN*: H [H_rows, K]
@@ -88,9 +86,11 @@ struct GemmParams {
   int has_shared;
   int K;
   int N;
-  int mt_max;                 // row-tile slots in the grid
+  int mt_max;                 // upper bound of the row tiles (grid size)
   int nt;                     // weight tiles
-  int ksplit;                 // K ranges (DOWN only)
+  int split_max;              // K ranges a tail tile may be cut into (1: none)
+  int kunit;                  // K steps of BK per unit of the schedule
+  int slots;                  // workgroups one XCD runs at once
   int krot;                   // rotate each workgroup's K order (spreads L2 channels)
   int cache_aux;              // cache-policy bits of the operand loads
 };
@@ -173,37 +173,17 @@ struct TileMap {
   bool shared_e;
 };
 
-// XCD-aware tile order, then the row-tile slot -> (expert, first row) map
-// read from the device-side offsets.  Returns false when the workgroup has
-// no tile.  Must be called by all threads of the workgroup.
+// The workgroup's unit of the tile schedule (tile_sched.h), then the
+// row-tile slot -> (expert, first row) map, both read from the device-side
+// offsets.  Returns false when the workgroup has no unit.  Must be called by
+// all threads of the workgroup.
 template <int MODE, int BM>
 __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   __shared__ int s_scan[4];
   __shared__ int s_info[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of logical tiles, ordered in GROUP_M x GROUP_N blocks
-  // (row-tile groups fastest), so an XCD's concurrent workgroups share both
-  // operands in its L2.
-  const int ksplit = (MODE == MODE_GATEUP) ? 1 : p.ksplit;
-  const int mgroups = (p.mt_max + GROUP_M - 1) / GROUP_M;
-  const int ngroups = (p.nt + GROUP_N - 1) / GROUP_N;
-  const int64_t tiles_per_k = (int64_t)mgroups * ngroups * (GROUP_M * GROUP_N);
-  const int64_t G = tiles_per_k * ksplit;
-  const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
-  const int64_t Lg = (int64_t)(blockIdx.x % NUM_XCD) * chunk + blockIdx.x / NUM_XCD;
-  if (Lg >= G) return false;
-  const int ks = (int)(Lg / tiles_per_k);
-  const int64_t L = Lg % tiles_per_k;
-  const int64_t blk = L / (GROUP_M * GROUP_N);
-  const int rr = (int)(L % (GROUP_M * GROUP_N));
-  // (uniform values computed with 64-bit VALU arithmetic: pin them to scalar
-  // registers so the buffer resources and offsets built from them need no
-  // per-lane loops)
-  const int mslot = __builtin_amdgcn_readfirstlane((int)(blk % mgroups) * GROUP_M + rr % GROUP_M);
-  const int ntile = __builtin_amdgcn_readfirstlane((int)(blk / mgroups) * GROUP_N + rr / GROUP_M);
-  if (mslot >= p.mt_max || ntile >= p.nt) return false;
 
+  // row tiles per segment (routed experts, then the shared expert), scanned
   const int nseg = p.E + (p.has_shared ? 1 : 0);
   const int per = (nseg + 255) / 256;
   const int e_lo = tid * per;
@@ -220,9 +200,21 @@ __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   __syncthreads();
   int before = 0;
   for (int w2 = 0; w2 < wave; ++w2) before += s_scan[w2];
-  const int total = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+  const int Mreal = __builtin_amdgcn_readfirstlane(s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3]);
+
+  // (uniform values: pin them to scalar registers so the buffer resources and
+  // offsets built from them need no per-lane loops)
+  SchedUnit u{};
+  const int kunits = p.K / BK / p.kunit;
+  if (!sched_unit(Mreal, p.nt, kunits, p.slots, p.split_max, (int)(blockIdx.x % kNumXcd),
+                  (int64_t)(blockIdx.x / kNumXcd), u))
+    return false;
+  const int mslot = __builtin_amdgcn_readfirstlane(u.mslot);
+  t.ntile = __builtin_amdgcn_readfirstlane(u.ntile);
+  t.kbeg = __builtin_amdgcn_readfirstlane(u.kbeg * p.kunit);
+  t.nk = __builtin_amdgcn_readfirstlane(u.nk * p.kunit);
+
   int excl = before + incl - local;
-  if (tid == 0 && mslot >= total) s_info[0] = -1;
   if (mslot >= excl && mslot < excl + local) {
     for (int i = 0; i < per; ++i) {
       const int e = e_lo + i;
@@ -242,16 +234,10 @@ __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   __syncthreads();
   // The LDS values are the same in every lane.
   t.e = __builtin_amdgcn_readfirstlane(s_info[0]);
-  if (t.e < 0) return false;
   t.m0 = __builtin_amdgcn_readfirstlane(s_info[1]);
   t.rows = __builtin_amdgcn_readfirstlane(s_info[2]);
   t.seg = __builtin_amdgcn_readfirstlane(s_info[3]);
-  t.ntile = ntile;
   t.shared_e = (t.e == p.E);
-  const int ksteps_all = p.K / BK;
-  t.kbeg = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps_all * ks / ksplit));
-  const int kend = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps_all * (ks + 1) / ksplit));
-  t.nk = kend - t.kbeg;
   return true;
 }
 
@@ -752,41 +738,55 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// Workgroups one XCD runs at once for a kernel of 256 threads and `lds`
+// bytes of LDS (after its LDS opt-in).
+int xcd_slots(const void* kernel, size_t lds) {
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, lds) != hipSuccess)
+    occ = 1;
+  return std::max(1, cus / kNumXcd) * std::max(1, occ);
+}
+
+// Grid of the tile schedule: kNumXcd x the bound of any XCD's units.
+inline unsigned sched_grid(const GemmParams& p) {
+  return (unsigned)(kNumXcd * sched_units_bound((int64_t)p.mt_max * p.nt, p.slots));
+}
+
 template <int MODE, bool FP8, int BM>
-hipError_t launch_gemm(const GemmParams& p, hipStream_t st) {
-  if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
-  const int64_t mg = (p.mt_max + GROUP_M - 1) / GROUP_M;
-  const int64_t ng = (p.nt + GROUP_N - 1) / GROUP_N;
-  const int64_t G = mg * ng * GROUP_M * GROUP_N * (MODE == MODE_GATEUP ? 1 : p.ksplit);
-  static bool attr_set = false;  // opt in to more than 64 KiB of LDS, once per process
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, FP8, BM>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
+  if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
+  const void* kern = (const void*)grouped_gemm_kernel<MODE, FP8, BM>;
+  static int slots = 0;  // opt in to more than 64 KiB of LDS, once per process
+  if (!slots) {
+    hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)Tile<BM>::LDS);
     if (err != hipSuccess) return err;
-    attr_set = true;
+    slots = xcd_slots(kern, Tile<BM>::LDS);
   }
-  const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
-  grouped_gemm_kernel<MODE, FP8, BM><<<(unsigned)(chunk * NUM_XCD), 256, Tile<BM>::LDS, st>>>(p);
+  GemmParams p = p0;
+  p.kunit = 1;
+  p.slots = slots;
+  grouped_gemm_kernel<MODE, FP8, BM><<<sched_grid(p), 256, Tile<BM>::LDS, st>>>(p);
   return hipGetLastError();
 }
 
 template <int MODE, int KB, int NS, int AUX = 0>
-hipError_t launch_gemm_dma_cfg(const GemmParams& p, hipStream_t st) {
-  const int64_t mg = (p.mt_max + GROUP_M - 1) / GROUP_M;
-  const int64_t ng = (p.nt + GROUP_N - 1) / GROUP_N;
-  const int64_t G = mg * ng * GROUP_M * GROUP_N * (MODE == MODE_GATEUP ? 1 : p.ksplit);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, KB, NS, AUX>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+hipError_t launch_gemm_dma_cfg(const GemmParams& p0, hipStream_t st) {
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, AUX>;
+  static int slots = 0;
+  if (!slots) {
+    hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)DmaCfg<KB, NS>::LDS);
     if (err != hipSuccess) return err;
-    attr_set = true;
+    slots = xcd_slots(kern, DmaCfg<KB, NS>::LDS);
   }
-  const int64_t chunk = (G + NUM_XCD - 1) / NUM_XCD;
-  grouped_gemm_dma_kernel<MODE, KB, NS, AUX>
-      <<<(unsigned)(chunk * NUM_XCD), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
+  GemmParams p = p0;
+  p.kunit = KB / BK;
+  p.slots = slots;
+  grouped_gemm_dma_kernel<MODE, KB, NS, AUX><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
   return hipGetLastError();
 }
 
@@ -796,8 +796,7 @@ template <int MODE>
 hipError_t launch_gemm_dma(const GemmParams& p, hipStream_t st) {
   if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
   const char* v = getenv("MOE_GEMM_DMA_CFG");
-  const int ksteps = p.K / BK;  // whole-K steps of 32
-  const bool k64_ok = (ksteps % (2 * (MODE == MODE_GATEUP ? 1 : p.ksplit)) == 0);
+  const bool k64_ok = (p.K / BK) % 2 == 0;
   if (v && !strcmp(v, "32x3")) return launch_gemm_dma_cfg<MODE, 32, 3>(p, st);
   if (v && !strcmp(v, "32x4")) return launch_gemm_dma_cfg<MODE, 32, 4>(p, st);
   if (k64_ok) {
@@ -870,7 +869,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.E = s.E;
   g.has_shared = has_sh;
   g.mt_max = (int)mt_bound(bm1);
-  g.ksplit = 1;
+  g.split_max = 1;
   {
     const char* kr = getenv("MOE_GEMM_KROT");
     const char* ax = getenv("MOE_GEMM_AUX");
@@ -910,18 +909,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   const int bn2 = 65536 / bm2;  // output columns per down tile
   g2.nt = (s.d + bn2 - 1) / bn2;
   g2.mt_max = (int)mt_bound(bm2);
-  // Split K only when the tile grid is small (decode-sized T), so that every
-  // CU streams weights; only with the atomic combine, whose adds also take the
-  // partial sums.  (On large grids the extra atomic passes into y cost more
-  // than the fuller last round of tiles gains.)
-  if (y) {
-    const int64_t est_rows_tiles = L.P_max / bm2 + (s.E + 1) / 2 + (has_sh ? (s.T + bm2 - 1) / bm2 : 0);
-    const int64_t tiles = std::max<int64_t>(1, std::min<int64_t>(est_rows_tiles, g2.mt_max)) * g2.nt;
-    const int ks_max = std::max(1, s.d_ff / BK / 8);
-    int ks = 1;
-    while (tiles * ks < 512 && ks * 2 <= ks_max) ks *= 2;
-    g2.ksplit = ks;
-  }
+  // With the atomic combine, partial sums over K ranges add up in y, so the
+  // tiles of the last, partial round of the schedule may be split over K
+  // (pieces of at least 8 steps).
+  g2.split_max = y ? std::max(1, s.d_ff / BK / 8) : 1;
   if (y)
     return bm2 == 256 ? launch_gemm_dt<MODE_DOWN, 256>(g2, fp8, st)
                       : launch_gemm_dt<MODE_DOWN, 128>(g2, fp8, st);

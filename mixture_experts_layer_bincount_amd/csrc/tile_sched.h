@@ -1,0 +1,103 @@
+// Work schedule of the grouped expert GEMMs: which output tile (and which
+// range of K) a workgroup computes.
+//
+// The number of row tiles is only known on the device (it depends on the
+// per-expert counts that the dispatch wrote), so every workgroup derives its
+// unit from the device-side total:
+//
+//  * Real tiles are numbered densely, q = 0 .. R-1 with R = Mreal * nt
+//    (Mreal row tiles summed over the expert segments, nt weight tiles), in
+//    blocks of GROUP_M row tiles x GROUP_N weight tiles, row tiles fastest, so
+//    that consecutive q share both operands.
+//  * Workgroup ids are dealt round-robin to the XCDs; XCD x takes the
+//    contiguous q range [R x / X, R (x+1) / X), so every XCD gets the same
+//    number of tiles (+-1) and its concurrent workgroups stay inside one or
+//    two operand blocks.
+//  * An XCD runs `slots` workgroups at once.  Its tiles fill
+//    floor(n / slots) whole rounds; when splitting is allowed (partial sums
+//    that are added, as the atomic combine does) the tiles of the last,
+//    partial round are cut into S K-ranges with rem * S <= slots, so the tail
+//    round takes 1/S of a tile's time instead of a whole one.
+//
+// Everything here is constexpr (callable from host and device code) and
+// free of HIP types, so the arithmetic is checked by a host-compiled test.
+#pragma once
+
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroupM = 8;  // row tiles per operand block
+constexpr int kGroupN = 4;  // weight tiles per operand block
+constexpr int kNumXcd = 8;  // XCDs of an MI355X; workgroups are dealt round-robin
+
+struct SchedUnit {
+  int mslot;  // row tile, 0 .. Mreal-1 (in segment order)
+  int ntile;  // weight tile, 0 .. nt-1
+  int kbeg;   // first K unit
+  int nk;     // K units
+};
+
+// Tile q -> (row tile, weight tile) in the blocked order described above.
+constexpr void sched_tile_of(int64_t q, int Mreal, int nt, int& mslot, int& ntile) {
+  const int64_t col = (int64_t)Mreal * kGroupN;  // tiles per full block column
+  const int ng = (int)(q / col);
+  const int64_t r = q - (int64_t)ng * col;
+  const int nh = (nt - ng * kGroupN) < kGroupN ? (nt - ng * kGroupN) : kGroupN;
+  const int mg = (int)(r / ((int64_t)kGroupM * nh));
+  const int r2 = (int)(r - (int64_t)mg * kGroupM * nh);
+  const int mh = (Mreal - mg * kGroupM) < kGroupM ? (Mreal - mg * kGroupM) : kGroupM;
+  mslot = mg * kGroupM + r2 % mh;
+  ntile = ng * kGroupN + r2 / mh;
+}
+
+// The K-range split of the tail round: pieces per tile for `rem` tiles on
+// `slots` concurrent workgroups, at most `split_max`.
+constexpr int sched_tail_split(int rem, int slots, int split_max) {
+  if (rem <= 0) return 1;
+  int s = slots / rem;
+  if (s > split_max) s = split_max;
+  return s < 1 ? 1 : s;
+}
+
+// Units one XCD runs (tiles of its whole rounds plus split tail pieces).
+constexpr int64_t sched_units_of_xcd(int64_t R, int xcd, int slots, int split_max) {
+  const int64_t q0 = R * xcd / kNumXcd, q1 = R * (xcd + 1) / kNumXcd;
+  const int64_t n = q1 - q0;
+  const int64_t full = n / slots * slots;
+  const int rem = (int)(n - full);
+  return full + (int64_t)rem * sched_tail_split(rem, slots, split_max);
+}
+
+// Upper bound of the units of any XCD given an upper bound of R (grid size).
+constexpr int64_t sched_units_bound(int64_t R_max, int slots) {
+  return (R_max + kNumXcd - 1) / kNumXcd + slots;
+}
+
+// Unit of workgroup `i` of XCD `xcd`.  kunits: K units of a whole tile.
+// Returns false when the workgroup has nothing to do.
+constexpr bool sched_unit(int Mreal, int nt, int kunits, int slots, int split_max, int xcd,
+                          int64_t i, SchedUnit& u) {
+  const int64_t R = (int64_t)Mreal * nt;
+  const int64_t q0 = R * xcd / kNumXcd, q1 = R * (xcd + 1) / kNumXcd;
+  const int64_t n = q1 - q0;
+  const int64_t full = n / slots * slots;
+  int64_t q = 0;
+  int piece = 0, S = 1;
+  if (i < full) {
+    q = q0 + i;
+  } else {
+    const int rem = (int)(n - full);
+    S = sched_tail_split(rem, slots, split_max);
+    const int64_t j = i - full;
+    if (j >= (int64_t)rem * S) return false;
+    q = q0 + full + j / S;
+    piece = (int)(j % S);
+  }
+  sched_tile_of(q, Mreal, nt, u.mslot, u.ntile);
+  u.kbeg = (int)((int64_t)kunits * piece / S);
+  u.nk = (int)((int64_t)kunits * (piece + 1) / S) - u.kbeg;
+  return true;
+}
+
+}  // namespace moe

@@ -73,6 +73,7 @@ def cpu_baseline(wl, host_experts, n_tokens: int) -> dict:
     (routing, dispatch, masked per-expert loop, combine; float64)."""
     import oracle
     c = wl.cfg
+    n_tokens = min(n_tokens, c.T)
     x = wl.x()[:n_tokens]
     W_g = wl.W_g()
     t0 = time.perf_counter()
@@ -89,11 +90,11 @@ def cpu_baseline(wl, host_experts, n_tokens: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -192,7 +193,7 @@ def main() -> int:
         "layer_tflops": flops_ffn / (ms_per_step * 1e-3) / 1e12,
         "stage_ms": stages,
         "counts": counts,
-        "roofline": {"kernel": "grouped_gemm_kernel<GATEUP> (gate/up GEMM + SwiGLU)",
+        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (grouped_gemm_dma_kernel<GATEUP>)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic,

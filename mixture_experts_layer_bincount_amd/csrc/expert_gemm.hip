@@ -31,6 +31,7 @@
 // workgroups one XCD runs at the same time share both operands in its L2;
 // with the atomic combine the tiles of the last, partial round are split over
 // K and their partial sums added by the same atomics.
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -91,6 +92,7 @@ struct GemmParams {
   int split_max;              // K ranges a tail tile may be cut into (1: none)
   int kunit;                  // K steps of BK per unit of the schedule
   int slots;                  // workgroups one XCD runs at once
+  int group_m, group_n;       // operand block of the tile order (row x weight tiles)
   int krot;                   // rotate each workgroup's K order (spreads L2 channels)
   int cache_aux;              // cache-policy bits of the operand loads
 };
@@ -206,7 +208,8 @@ __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   // offsets built from them need no per-lane loops)
   SchedUnit u{};
   const int kunits = p.K / BK / p.kunit;
-  if (!sched_unit(Mreal, p.nt, kunits, p.slots, p.split_max, (int)(blockIdx.x % kNumXcd),
+  if (!sched_unit(Mreal, p.nt, p.group_m, p.group_n, kunits, p.slots, p.split_max,
+                  (int)(blockIdx.x % kNumXcd),
                   (int64_t)(blockIdx.x / kNumXcd), u))
     return false;
   const int mslot = __builtin_amdgcn_readfirstlane(u.mslot);
@@ -563,7 +566,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX>
+// s_waitcnt with only the LDS counter constrained: lgkmcnt(0).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+template <int MODE, int KB, int NS, int MOE_AUX, bool IL>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   using C = DmaCfg<KB, NS>;
   constexpr int BNB = 256;
@@ -662,6 +670,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     });
   };
 
+  if constexpr (!IL) {
   // ---- pipeline.  Before computing step kt a wave waits until its own DMA
   // for step kt has landed (the DMA of the following steps already issued
   // may still be in flight), then a barrier makes every wave's part visible
@@ -684,6 +693,87 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
       compute(kt % NS);
     }
+  }
+  } else {
+  // ---- interleaved pipeline over 32-deep K slices (HPS per DMA step).  The
+  // fragments of slice s + 1 are read from LDS while the MFMAs of slice s run
+  // (two fragment buffers, one read between every two MFMAs).  Before the
+  // first read of a new step t, each wave has finished its reads of step
+  // t - 1 (lgkmcnt 0) and waited for its own DMA of step t; one barrier then
+  // makes step t visible to all waves and frees the stage of step t - 1, which
+  // is refilled with step t + NS - 1.
+  constexpr int HPS = KB / 32;
+  const int nsl = nk * HPS;
+  // per-lane LDS byte offsets of the fragment rows (stage 0, chunk slot 0)
+  // and of the swizzled 16-byte chunk for each (half, kk) of a step
+  const int a_row_off = (arow0 + frow) * C::RB;
+  int col_off[HPS][2];
+  static_for<HPS>([&](auto h) {
+    static_for<2>([&](auto kk) { col_off[h][kk] = (((h * 4 + kk * 2 + fhalf) ^ swz) * 16); });
+  });
+  bf16x8 fa0[2][4], fb0[2][4], fa1[2][4], fb1[2][4];
+  auto read_slice = [&](int sl, bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4]) __attribute__((always_inline)) {
+    const int stage = (sl / HPS) % NS;
+    const int h = sl % HPS;
+    const char* a = dlds + stage * C::STAGE_BYTES;
+    const char* b = a + C::TILE_BYTES;
+    static_for<2>([&](auto kk) {
+      const int co = (HPS == 1 || h == 0) ? col_off[0][kk] : col_off[HPS - 1][kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[kk][i] = *(const bf16x8*)(a + a_row_off + i * 32 * C::RB + co);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
+    });
+  };
+  // step boundary before slice sl (sl % HPS == 0, sl > 0): see above
+  auto step_sync = [&](int sl) __attribute__((always_inline)) {
+    const int t = sl / HPS;
+    wait_lgkm0();
+    // steady state: the NS - 2 later steps may stay in flight; near the end
+    // (fewer issued) wait for everything
+    if (t + NS - 2 <= nk - 1)
+      wait_vmcnt<(NS - 2) * C::NI>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t + NS - 1 < nk) issue(t + NS - 1, (t + NS - 1) % NS);
+  };
+  // MFMAs of one slice from (fa, fb) with the reads of slice `next` into
+  // (ga, gb) interleaved.  `next` may be past the end: it then rereads a
+  // valid stage and the values go unused.
+  auto slice = [&](bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4], int next, bf16x8 (&ga)[2][4],
+                   bf16x8 (&gb)[2][4]) __attribute__((always_inline)) {
+    read_slice(next < nsl ? next : nsl - 1, ga, gb);
+    mfma_slice<MODE>(acc, fa[0], fb[0]);
+    mfma_slice<MODE>(acc, fa[1], fb[1]);
+    static_for<16>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+    });
+  };
+  if (nk > 0) {
+    static_for<NS - 1>([&](auto s) {
+      if (s < nk) issue(s, s);
+    });
+    if (NS - 2 >= 2 && nk > 2)
+      wait_vmcnt<2 * C::NI>();
+    else if (NS - 2 >= 1 && nk > 1)
+      wait_vmcnt<C::NI>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (NS - 1 < nk) issue(NS - 1, (NS - 1) % NS);
+    read_slice(0, fa0, fb0);
+    // two slices per iteration (fragment buffers 0 and 1); single exit
+    int sl = 0;
+    for (; sl + 2 <= nsl; sl += 2) {
+      if ((sl + 1) % HPS == 0) step_sync(sl + 1);
+      slice(fa0, fb0, sl + 1, fa1, fb1);
+      if ((sl + 2) % HPS == 0 && sl + 2 < nsl) step_sync(sl + 2);
+      slice(fa1, fb1, sl + 2, fa0, fb0);
+    }
+    if (sl < nsl) slice(fa0, fb0, nsl, fa1, fb1);
+  }
   }
   store_tile<MODE, false>(p, acc, t, arow0, n0, wn, brow);
 }
@@ -773,9 +863,9 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE, int KB, int NS, int AUX = 0>
+template <int MODE, int KB, int NS, bool IL>
 hipError_t launch_gemm_dma_cfg(const GemmParams& p0, hipStream_t st) {
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, AUX>;
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, IL>;
   static int slots = 0;
   if (!slots) {
     hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -786,25 +876,24 @@ hipError_t launch_gemm_dma_cfg(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
-  grouped_gemm_dma_kernel<MODE, KB, NS, AUX><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1, IL><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
   return hipGetLastError();
 }
 
-// DMA pipeline shape: K per stage x stages (MOE_GEMM_DMA_CFG=32x4|32x3|64x2
-// for tuning).  A K range that is not a multiple of 64 takes 32-deep steps.
+// DMA pipeline shape: 64-deep steps in two stages, or 32-deep steps in four
+// (MOE_GEMM_DMA_CFG=32x4, and always when K is not a multiple of 64);
+// the interleaved fragment pipeline unless MOE_GEMM_IL=0.
 template <int MODE>
 hipError_t launch_gemm_dma(const GemmParams& p, hipStream_t st) {
   if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
   const char* v = getenv("MOE_GEMM_DMA_CFG");
-  const bool k64_ok = (p.K / BK) % 2 == 0;
-  if (v && !strcmp(v, "32x3")) return launch_gemm_dma_cfg<MODE, 32, 3>(p, st);
-  if (v && !strcmp(v, "32x4")) return launch_gemm_dma_cfg<MODE, 32, 4>(p, st);
-  if (k64_ok) {
-    if (p.cache_aux == 1) return launch_gemm_dma_cfg<MODE, 64, 2, 1>(p, st);
-    if (p.cache_aux == 2) return launch_gemm_dma_cfg<MODE, 64, 2, 2>(p, st);
-    return launch_gemm_dma_cfg<MODE, 64, 2>(p, st);
-  }
-  return launch_gemm_dma_cfg<MODE, 32, 4>(p, st);
+  const char* il = getenv("MOE_GEMM_IL");
+  const bool IL = !(il && atoi(il) == 0);
+  const bool k64 = (p.K / BK) % 2 == 0 && !(v && !strcmp(v, "32x4"));
+  if (k64) return IL ? launch_gemm_dma_cfg<MODE, 64, 2, true>(p, st)
+                     : launch_gemm_dma_cfg<MODE, 64, 2, false>(p, st);
+  return IL ? launch_gemm_dma_cfg<MODE, 32, 4, true>(p, st)
+            : launch_gemm_dma_cfg<MODE, 32, 4, false>(p, st);
 }
 
 // bf16 weights with 256-row tiles take the LDS-DMA kernel unless
@@ -875,6 +964,16 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
     const char* ax = getenv("MOE_GEMM_AUX");
     g.krot = kr ? atoi(kr) : 0;
     g.cache_aux = ax ? atoi(ax) : 1;
+    const char* gr = getenv("MOE_GEMM_GROUP");  // "MxN" (tuning)
+    g.group_m = 8;
+    g.group_n = 4;
+    if (gr) {
+      int gm = 0, gn = 0;
+      if (sscanf(gr, "%dx%d", &gm, &gn) == 2 && gm > 0 && gn > 0) {
+        g.group_m = gm;
+        g.group_n = gn;
+      }
+    }
   }
 
   // gate / up

@@ -7,8 +7,8 @@
 //
 //  * Real tiles are numbered densely, q = 0 .. R-1 with R = Mreal * nt
 //    (Mreal row tiles summed over the expert segments, nt weight tiles), in
-//    blocks of GROUP_M row tiles x GROUP_N weight tiles, row tiles fastest, so
-//    that consecutive q share both operands.
+//    blocks of gm row tiles x gn weight tiles, row tiles fastest, so that
+//    consecutive q share both operands.
 //  * Workgroup ids are dealt round-robin to the XCDs; XCD x takes the
 //    contiguous q range [R x / X, R (x+1) / X), so every XCD gets the same
 //    number of tiles (+-1) and its concurrent workgroups stay inside one or
@@ -27,8 +27,6 @@
 
 namespace moe {
 
-constexpr int kGroupM = 8;  // row tiles per operand block
-constexpr int kGroupN = 4;  // weight tiles per operand block
 constexpr int kNumXcd = 8;  // XCDs of an MI355X; workgroups are dealt round-robin
 
 struct SchedUnit {
@@ -38,17 +36,19 @@ struct SchedUnit {
   int nk;     // K units
 };
 
-// Tile q -> (row tile, weight tile) in the blocked order described above.
-constexpr void sched_tile_of(int64_t q, int Mreal, int nt, int& mslot, int& ntile) {
-  const int64_t col = (int64_t)Mreal * kGroupN;  // tiles per full block column
+// Tile q -> (row tile, weight tile) in the blocked order described above,
+// with blocks of gm row tiles x gn weight tiles.
+constexpr void sched_tile_of(int64_t q, int Mreal, int nt, int gm, int gn, int& mslot,
+                             int& ntile) {
+  const int64_t col = (int64_t)Mreal * gn;  // tiles per full block column
   const int ng = (int)(q / col);
   const int64_t r = q - (int64_t)ng * col;
-  const int nh = (nt - ng * kGroupN) < kGroupN ? (nt - ng * kGroupN) : kGroupN;
-  const int mg = (int)(r / ((int64_t)kGroupM * nh));
-  const int r2 = (int)(r - (int64_t)mg * kGroupM * nh);
-  const int mh = (Mreal - mg * kGroupM) < kGroupM ? (Mreal - mg * kGroupM) : kGroupM;
-  mslot = mg * kGroupM + r2 % mh;
-  ntile = ng * kGroupN + r2 / mh;
+  const int nh = (nt - ng * gn) < gn ? (nt - ng * gn) : gn;
+  const int mg = (int)(r / ((int64_t)gm * nh));
+  const int r2 = (int)(r - (int64_t)mg * gm * nh);
+  const int mh = (Mreal - mg * gm) < gm ? (Mreal - mg * gm) : gm;
+  mslot = mg * gm + r2 % mh;
+  ntile = ng * gn + r2 / mh;
 }
 
 // The K-range split of the tail round: pieces per tile for `rem` tiles on
@@ -76,8 +76,8 @@ constexpr int64_t sched_units_bound(int64_t R_max, int slots) {
 
 // Unit of workgroup `i` of XCD `xcd`.  kunits: K units of a whole tile.
 // Returns false when the workgroup has nothing to do.
-constexpr bool sched_unit(int Mreal, int nt, int kunits, int slots, int split_max, int xcd,
-                          int64_t i, SchedUnit& u) {
+constexpr bool sched_unit(int Mreal, int nt, int gm, int gn, int kunits, int slots,
+                          int split_max, int xcd, int64_t i, SchedUnit& u) {
   const int64_t R = (int64_t)Mreal * nt;
   const int64_t q0 = R * xcd / kNumXcd, q1 = R * (xcd + 1) / kNumXcd;
   const int64_t n = q1 - q0;
@@ -94,7 +94,7 @@ constexpr bool sched_unit(int Mreal, int nt, int kunits, int slots, int split_ma
     q = q0 + full + j / S;
     piece = (int)(j % S);
   }
-  sched_tile_of(q, Mreal, nt, u.mslot, u.ntile);
+  sched_tile_of(q, Mreal, nt, gm, gn, u.mslot, u.ntile);
   u.kbeg = (int)((int64_t)kunits * piece / S);
   u.nk = (int)((int64_t)kunits * (piece + 1) / S) - u.kbeg;
   return true;

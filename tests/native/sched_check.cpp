@@ -13,7 +13,7 @@
 
 using namespace moe;
 
-static int check(int Mreal, int nt, int kunits, int slots, int split_max) {
+static int check(int Mreal, int nt, int gm, int gn, int kunits, int slots, int split_max) {
   const int64_t R = (int64_t)Mreal * nt;
   std::vector<int> cover((size_t)R * kunits, 0);
   const int64_t per_xcd = sched_units_bound(R, slots);
@@ -21,7 +21,7 @@ static int check(int Mreal, int nt, int kunits, int slots, int split_max) {
     int64_t units = 0;
     for (int64_t i = 0; i < per_xcd + 3; ++i) {
       SchedUnit u{};
-      const bool ok = sched_unit(Mreal, nt, kunits, slots, split_max, x, i, u);
+      const bool ok = sched_unit(Mreal, nt, gm, gn, kunits, slots, split_max, x, i, u);
       if (!ok) continue;
       if (i >= per_xcd) {
         printf("FAIL unit beyond grid M=%d nt=%d x=%d i=%lld\n", Mreal, nt, x, (long long)i);
@@ -66,15 +66,17 @@ int main() {
     for (int nt : nts)
       for (int ku : kus)
         for (int sl : slotss)
-          for (int sp : splits) {
-            if (check(M, nt, ku, sl, sp < ku ? sp : ku)) return 1;
-            ++cases;
-          }
+          for (int sp : splits)
+            for (int g = 0; g < 3; ++g) {
+              const int gm = g == 0 ? 8 : g == 1 ? 4 : 1, gn = g == 0 ? 4 : g == 1 ? 8 : 16;
+              if (check(M, nt, gm, gn, ku, sl, sp < ku ? sp : ku)) return 1;
+              ++cases;
+            }
   // the blocked order: consecutive tiles of a full block share row tiles
   // within groups of 8 and weight tiles within groups of 4
   for (int64_t q = 0; q < 32; ++q) {
     int m = 0, n = 0;
-    sched_tile_of(q, 40, 112, m, n);
+    sched_tile_of(q, 40, 112, 8, 4, m, n);
     if (m != (int)(q % 8) || n != (int)(q / 8)) {
       printf("FAIL block order q=%lld -> %d %d\n", (long long)q, m, n);
       return 1;

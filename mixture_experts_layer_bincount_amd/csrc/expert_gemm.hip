@@ -778,6 +778,163 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   store_tile<MODE, false>(p, acc, t, arow0, n0, wn, brow);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for few rows per expert (decode-sized batches).
+// With ~16 rows per expert the GEMMs are bound by reading the weights once
+// from HBM; tiles of 128 or 256 rows would spend most MFMAs on padding and
+// keep too few bytes in flight.  Here every wave owns 16 weight rows
+// (16 output features) of one expert and walks K in steps of 32, loading its
+// weight fragments straight from global memory into MFMA operand registers
+// (16x16x32 bf16: lane l holds 8 consecutive K of weight row l % 16), D steps
+// ahead, with no LDS and no barriers.  The expert's activation rows (at most
+// 16 * RG per pass; more rows take further passes) come through the same
+// kind of fragment loads and stay cache-resident, as every wave of the
+// expert reads the same rows.  The product is computed transposed (weights
+// as the A operand), so lane l ends with activation row l % 16 and 4
+// consecutive output features 4 (l / 16) .. + 3.
+//   GATEUP  W1 and W3 rows of the same 16 hidden features; SwiGLU in registers
+//   DOWN    W2 rows of 16 output features; K may be split over workgroups
+//           (p.split_max pieces), whose partial sums the atomic combine adds
+//   DOWN_PERM  as DOWN into the grouped output (K not split)
+// Workgroup b: segment (expert, or E for the shared expert), a block of 64
+// output features (4 waves x 16) and a K piece.
+template <bool FP8>
+__device__ __forceinline__ bf16x8 load_w8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  const uint4 v = load_b8<FP8>(r, voff, soff);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int MODE, bool FP8, int RG, int D>
+__global__ __launch_bounds__(256) void grouped_stream_kernel(GemmParams p) {
+  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int K = p.K, N = p.N;
+  const int ncb = (N + 63) / 64;
+  const int ks = (MODE == MODE_DOWN) ? p.split_max : 1;
+  int b = (int)blockIdx.x;
+  const int kp = b % ks;
+  b /= ks;
+  const int cb = b % ncb;
+  const int e = b / ncb;  // segment
+  const bool shared_e = (e == p.E);
+  const int rows = shared_e ? (int)p.T : p.offsets[e + 1] - p.offsets[e];
+  const int seg = shared_e ? 0 : p.offsets[e];
+  const int n0 = cb * 64 + wave * 16;
+  if (rows <= 0 || n0 >= N) return;
+  const int ksteps = K / 32;
+  const int kbeg = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps * kp / ks));
+  const int nk = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps * (kp + 1) / ks) - kbeg);
+
+  const int64_t ebytes = (int64_t)N * K * WB;
+  const int64_t eoff = shared_e ? 0 : (int64_t)e * ebytes;
+  const __amdgpu_buffer_rsrc_t rsW0 =
+      uniform_rsrc((const char*)(shared_e ? p.B0s : p.B0) + eoff, ebytes);
+  __amdgpu_buffer_rsrc_t rsW1 = rsW0;
+  if (MODE == MODE_GATEUP)
+    rsW1 = uniform_rsrc((const char*)(shared_e ? p.B1s : p.B1) + eoff, ebytes);
+  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A, p.A_bytes);
+  const int fr = lane & 15;         // fragment row: weight row / activation row
+  const int fk = (lane >> 4) * 8;   // first K element of the lane within a step
+  const uint32_t voW = (uint32_t)(((int64_t)(n0 + fr) * K + (int64_t)kbeg * 32 + fk) * WB);
+
+  float sc0 = 1.f, sc1 = 1.f;
+  if (FP8) {
+    const int gi = n0 / kFp8Group;  // the wave's 16 rows share one scale
+    sc0 = shared_e ? p.sc0s[gi] : p.sc0[(int64_t)e * (N / kFp8Group) + gi];
+    if (MODE == MODE_GATEUP) sc1 = shared_e ? p.sc1s[gi] : p.sc1[(int64_t)e * (N / kFp8Group) + gi];
+  }
+
+  const int krot = p.krot ? __builtin_amdgcn_readfirstlane(
+                                (int)((((unsigned)blockIdx.x * 4u + wave) * 2654435761u >> 8) %
+                                      (unsigned)nk))
+                          : 0;
+  for (int r0 = 0; r0 < rows; r0 += 16 * RG) {
+    uint32_t voA[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const int m = min(r0 + g * 16 + fr, rows - 1);
+      voA[g] = (uint32_t)((a_row<MODE>(p, TileMap{e, 0, rows, seg, 0, 0, 0, shared_e}, m) * K +
+                           (int64_t)kbeg * 32 + fk) * 2);
+    }
+    f32x4 acc0[RG], acc1[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bf16x8 w0[D], w1[D], xa[D][RG];
+    // step s of this piece (clamped to the last step: the extra loads past
+    // the end reread data already in the caches and are never used), walked
+    // from a per-wave rotated start so that concurrent waves, whose weight
+    // rows lie a power-of-two stride apart, spread over the memory channels
+    auto load = [&](auto slot, int s) __attribute__((always_inline)) {
+      int st = min(s, nk - 1) + krot;
+      st = __builtin_amdgcn_readfirstlane(st >= nk ? st - nk : st);
+      w0[slot] = load_w8<FP8>(rsW0, voW, st * 32 * WB);
+      if (MODE == MODE_GATEUP) w1[slot] = load_w8<FP8>(rsW1, voW, st * 32 * WB);
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        xa[slot][g] = __builtin_bit_cast(bf16x8, buf_load16(rsA, voA[g], st * 64));
+    };
+    auto mma = [&](auto slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0[slot], xa[slot][g], acc0[g], 0, 0, 0);
+        if (MODE == MODE_GATEUP)
+          acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1[slot], xa[slot][g], acc1[g], 0, 0, 0);
+      }
+    };
+    static_for<D>([&](auto s) { load(s, s); });
+    int kt = 0;
+    for (; kt + D <= nk; kt += D) {  // single exit; slots stay compile-time
+      static_for<D>([&](auto s) {
+        mma(s);
+        load(s, kt + s + D);
+      });
+    }
+    static_for<D>([&](auto s) {
+      if (kt + s < nk) mma(s);
+    });
+
+    // epilogue: lane holds activation row r0 + 16 g + fr, features n0 + fk/2 .. + 3
+    const int nf = n0 + (lane >> 4) * 4;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const int m = r0 + g * 16 + fr;
+      if (m >= rows) continue;
+      if (MODE == MODE_GATEUP) {
+        const int64_t hrow = (shared_e ? p.P_max : (int64_t)seg) + m;
+        uint32_t hb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = acc0[g][r] * sc0;
+          const float u = acc1[g][r] * sc1;
+          hb[r] = f32_to_bf16_bits(a / (1.f + __expf(-a)) * u);
+        }
+        uint2 v;
+        v.x = hb[0] | (hb[1] << 16);
+        v.y = hb[2] | (hb[3] << 16);
+        *(uint2*)(p.H + hrow * N + nf) = v;
+      } else if (MODE == MODE_DOWN) {
+        int64_t orow = m;
+        float wgt = 1.f;
+        if (!shared_e) {
+          orow = p.perm_token[seg + m];
+          wgt = p.perm_w[seg + m] * sc0;
+        } else {
+          wgt = sc0;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) atomicAdd(&p.y[orow * N + nf + r], wgt * acc0[g][r]);
+      } else {
+        float4 v = make_float4(acc0[g][0] * sc0, acc0[g][1] * sc0, acc0[g][2] * sc0, acc0[g][3] * sc0);
+        *(float4*)(p.y_perm + ((int64_t)seg + m) * N + nf) = v;
+      }
+    }
+  }
+}
+
 // Linear+bias experts in fp32 (the tutorial's nn.Linear(d, d) experts, §4.1).
 // One thread per (grouped row, output feature); MODE_DOWN adds w * out into y.
 template <int MODE>
@@ -906,6 +1063,23 @@ hipError_t launch_gemm_dt(const GemmParams& p, bool fp8, hipStream_t st) {
   return launch_gemm<MODE, false, BM>(p, st);
 }
 
+// Weight-streaming launch: one workgroup per (segment, 64 output features,
+// K piece); p.split_max = K pieces (MODE_DOWN only).
+template <int MODE, bool FP8>
+hipError_t launch_stream(const GemmParams& p, int nseg, hipStream_t st) {
+  const int64_t grid = (int64_t)nseg * ((p.N + 63) / 64) * (MODE == MODE_DOWN ? p.split_max : 1);
+  if (grid <= 0) return hipSuccess;
+  const char* dv = getenv("MOE_STREAM_D");  // prefetch depth (tuning)
+  const int D = dv ? atoi(dv) : 8;
+  if (D == 4)
+    grouped_stream_kernel<MODE, FP8, 2, 4><<<(unsigned)grid, 256, 0, st>>>(p);
+  else if (D == 12)
+    grouped_stream_kernel<MODE, FP8, 2, 12><<<(unsigned)grid, 256, 0, st>>>(p);
+  else
+    grouped_stream_kernel<MODE, FP8, 2, 8><<<(unsigned)grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 // Row-tile height of the grouped GEMMs: 256 (256 x 256 tiles; LDS-DMA kernel
 // for bf16 weights) by default, or 128 (128 x 512 tiles, register-staged);
 // MOE_GEMM_BM, MOE_GEMM_BM_GATEUP and MOE_GEMM_BM_DOWN override it (tuning).
@@ -986,8 +1160,22 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.N = s.d_ff;
   const int bn1 = 65536 / bm1 / 2;  // hidden columns per gate/up tile
   g.nt = (s.d_ff + bn1 - 1) / bn1;
-  hipError_t err = bm1 == 256 ? launch_gemm_dt<MODE_GATEUP, 256>(g, fp8, st)
-                              : launch_gemm_dt<MODE_GATEUP, 128>(g, fp8, st);
+  // Few rows per expert (decode): the weight-streaming kernel for the gate/up
+  // projection (MOE_STREAM=0 turns it off).  The tiled down projection with
+  // its K-split tail measures faster than the streaming one at decode size
+  // (MOE_STREAM_DOWN=1 selects the latter, for comparison).
+  const char* sv = getenv("MOE_STREAM");
+  const char* sdv = getenv("MOE_STREAM_DOWN");
+  const bool stream = rows_per_expert <= 32 && !(sv && atoi(sv) == 0);
+  const bool stream_down = stream && sdv && atoi(sdv) == 1;
+  const int nseg = s.E + has_sh;
+  hipError_t err;
+  if (stream)
+    err = fp8 ? launch_stream<MODE_GATEUP, true>(g, nseg, st)
+              : launch_stream<MODE_GATEUP, false>(g, nseg, st);
+  else
+    err = bm1 == 256 ? launch_gemm_dt<MODE_GATEUP, 256>(g, fp8, st)
+                     : launch_gemm_dt<MODE_GATEUP, 128>(g, fp8, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {
     err = hipEventRecord(ev_mid, st);
@@ -1012,6 +1200,18 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // tiles of the last, partial round of the schedule may be split over K
   // (pieces of at least 8 steps).
   g2.split_max = y ? std::max(1, s.d_ff / BK / 8) : 1;
+  if (stream_down) {
+    // K pieces so that about 8192 waves stream W2 (each at least 16 steps)
+    const int64_t waves = (int64_t)nseg * ((s.d + 63) / 64) * 4;
+    int ks = (int)std::min<int64_t>(8, (8192 + waves - 1) / waves);
+    ks = std::max(1, std::min(ks, s.d_ff / 32 / 16));
+    g2.split_max = y ? ks : 1;
+    if (y)
+      return fp8 ? launch_stream<MODE_DOWN, true>(g2, nseg, st)
+                 : launch_stream<MODE_DOWN, false>(g2, nseg, st);
+    return fp8 ? launch_stream<MODE_DOWN_PERM, true>(g2, nseg, st)
+               : launch_stream<MODE_DOWN_PERM, false>(g2, nseg, st);
+  }
   if (y)
     return bm2 == 256 ? launch_gemm_dt<MODE_DOWN, 256>(g2, fp8, st)
                       : launch_gemm_dt<MODE_DOWN, 128>(g2, fp8, st);

@@ -34,6 +34,11 @@ SMALL = [
     (129, 768, 32, 8, 256, 0.5, True, "bf16", None),
     (500, 256, 8, 2, 256, None, True, "fp8_e4m3", None),
     (64, 512, 8, 2, 1408, None, False, "bf16", None),
+    # few rows per expert (the weight-streaming kernels): fp8, a shared
+    # expert that takes several 32-row passes, and a capacity limit
+    (64, 512, 8, 2, 1408, None, False, "fp8_e4m3", None),
+    (48, 256, 4, 2, 256, None, True, "bf16", None),
+    (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5"),
 ]
 
 
@@ -58,10 +63,12 @@ def test_tiny_page_layer(moe):
     print(f"[tiny] err={rep['err']:.3e} load={out['counts'].tolist()}", flush=True)
 
 
-def test_unfused_path_matches_fused(moe):
+@pytest.mark.parametrize("T,seed", [(600, 5), (64, 6)])
+def test_unfused_path_matches_fused(moe, T, seed):
     """moe_expert_ffn into a grouped output, then moe_combine, against the
-    fused scatter-add path and the oracle."""
-    cfg = custom_config(600, 256, 8, 2, 256, cf=1.0, seed=5)
+    fused scatter-add path and the oracle (600 tokens: tiled GEMMs; 64:
+    the weight-streaming kernels)."""
+    cfg = custom_config(T, 256, 8, 2, 256, cf=1.0, seed=seed)
     wl = Workload(cfg)
     out, layer, dev = gpu_forward(wl)
     s = layer.shape

@@ -171,8 +171,10 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
  *   y      [device] fp32 [T, d]: y[t] += perm_w[p] * expert_e(x[t]) for every grouped
  *          row (the combine fused into the last GEMM; y is NOT cleared here;
  *          the shared expert, if any, is added with weight 1 for every token)
- *   y_perm [device] fp32 [P_max, d]: y_perm[p] = expert_e(x[perm_token[p]]) (no
- *          weight; finish with moe_combine; shared experts are not allowed here)
+ *   y_perm [device] fp32 [P_max (+ T with a shared expert), d]:
+ *          y_perm[p] = expert_e(x[perm_token[p]]) (no weight) for p < P_max, and
+ *          y_perm[P_max + t] = shared(x[t]) when there is a shared expert; finish
+ *          with moe_combine
  *   x is the original [T, d] activation (rows are gathered on load). */
 moe_status moe_expert_ffn(const moe_shape* shape, const moe_weights* w,
                           const void* x, const int32_t* offsets,
@@ -181,14 +183,21 @@ moe_status moe_expert_ffn(const moe_shape* shape, const moe_weights* w,
 
 /* Combine (MOE 学习笔记 输出聚合: weighted sum of the chosen experts' outputs):
  * y[t] = sum over kept j of topk_w[t, j] * y_perm[slot_pos[t, j]], in slot
- * order; dropped assignments (slot_pos == -1) add nothing.  y [device] fp32
- * [T, d] is overwritten. */
+ * order, then + y_perm[P_max + t] (weight 1) with a shared expert; dropped
+ * assignments (slot_pos == -1) add nothing.  y_perm is laid out as
+ * moe_expert_ffn writes it; y [device] fp32 [T, d] is overwritten.  The sum
+ * order is fixed, so the result is deterministic. */
 moe_status moe_combine(const moe_shape* shape, const float* y_perm,
                        const int32_t* slot_pos, const float* topk_w, float* y,
                        void* stream);
 
-/* The whole layer: route, dispatch, grouped FFN with the fused combine,
- * shared expert.  y [device] fp32 [T, d] is overwritten.  topk_idx, topk_w,
+/* The whole layer: route, dispatch, grouped FFN, combine, shared expert.
+ * With few rows per expert (P_max / E <= 32, decode-sized batches) the
+ * combine is fused into the down projection as fp32 atomic adds into a
+ * cleared y, so that projection can split K over workgroups; otherwise the
+ * down projection writes a grouped fp32 output in the workspace and a
+ * combine pass sums each token's rows in slot order (no read-modify-write of
+ * y, and a deterministic result).  y [device] fp32 [T, d] is overwritten.  topk_idx, topk_w,
  * counts, offsets [device] are outputs as above; ws [device] holds
  * moe_workspace_bytes(shape) bytes.  No host synchronisation. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g,

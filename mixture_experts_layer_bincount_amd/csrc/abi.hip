@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -126,6 +127,7 @@ struct Ws {
   float* perm_w;
   int32_t* slot_pos;
   void* H;
+  float* Yp;
 };
 
 Ws carve(const WsLayout& L, void* ws) {
@@ -133,7 +135,7 @@ Ws carve(const WsLayout& L, void* ws) {
   return Ws{(float*)(b + L.off_partial),     (void*)(b + L.off_wsplit), (int32_t*)(b + L.off_chunk_hist),
             (int32_t*)(b + L.off_chunk_base), (int32_t*)(b + L.off_perm_token),
             (float*)(b + L.off_perm_w),       (int32_t*)(b + L.off_slot_pos),
-            (void*)(b + L.off_H)};
+            (void*)(b + L.off_H),             L.grouped_combine ? (float*)(b + L.off_Yp) : nullptr};
 }
 
 // ---- stage timing
@@ -199,8 +201,25 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
   L.off_H = off;
   if (s.kind == MOE_EXPERT_SWIGLU) off = align256(off + (size_t)L.H_rows * s.d_ff * 2);
+  L.grouped_combine = use_grouped_combine(s);
+  L.off_Yp = off;
+  if (L.grouped_combine) off = align256(off + (size_t)L.H_rows * s.d * sizeof(float));
   L.total = off;
   return L;
+}
+
+bool use_grouped_combine(const moe_shape& s) {
+  if (s.kind != MOE_EXPERT_SWIGLU) return false;
+  const char* v = getenv("MOE_COMBINE");  // "grouped" | "atomic" (comparison)
+  if (v && !strcmp(v, "grouped")) return true;
+  if (v && !strcmp(v, "atomic")) return false;
+  // Few rows per expert (decode): the atomic form, whose down projection may
+  // split K over workgroups; otherwise the grouped output (measured faster
+  // with many experts per token or a large y, equal at the Mixtral shape, and
+  // deterministic).
+  const int64_t A = s.T * (int64_t)s.top_k;
+  const int64_t P_max = (s.capacity < 0) ? A : std::min<int64_t>(A, (int64_t)s.E * s.capacity);
+  return P_max / s.E > 32;
 }
 
 }  // namespace moe
@@ -294,8 +313,6 @@ moe_status moe_expert_ffn(const moe_shape* shape, const moe_weights* w, const vo
   const moe_shape& s = *shape;
   if ((y_perm == nullptr) == (y == nullptr))
     return fail(MOE_ERR_INVALID, "exactly one of y_perm and y must be non-NULL");
-  if (y_perm && s.has_shared)
-    return fail(MOE_ERR_INVALID, "the grouped output (y_perm) has no rows for a shared expert");
   if (s.T == 0) return MOE_OK;
   MOE_TRY(check_weights(&s, w));
   MOE_TRY(check_ptr(x, "x", 16));
@@ -324,7 +341,8 @@ moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_
   MOE_TRY(check_ptr(slot_pos, "slot_pos"));
   MOE_TRY(check_ptr(topk_w, "topk_w"));
   MOE_TRY(check_ptr(y, "y"));
-  return hip_status(launch_combine(s, y_perm, slot_pos, topk_w, y, (hipStream_t)stream),
+  return hip_status(launch_combine(s, ws_layout(s).P_max, y_perm, slot_pos, topk_w, y,
+                                   (hipStream_t)stream),
                     "combine");
 }
 
@@ -363,6 +381,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
                                      W.perm_w, W.slot_pos, W.chunk_hist, W.chunk_base, st),
                      "dispatch"));
   ce.mark(3, st);
+  if (L.grouped_combine) {
+    // grouped fp32 output, then the combine kernel writes every element of y
+    ce.mark(4, st);
+    MOE_TRY(hip_status(launch_expert_ffn(s, L, *w, x, offsets, W.perm_token, W.perm_w, W.Yp,
+                                         nullptr, W.H, st, ce.at(5)),
+                       "expert ffn"));
+    const moe_status r = hip_status(
+        launch_combine(s, L.P_max, W.Yp, W.slot_pos, topk_w, y, st), "combine");
+    ce.mark(6, st);
+    ce.finish();
+    return r;
+  }
   MOE_TRY(hip_status(launch_fill_zero(y, s.T * (int64_t)s.d, st), "clear y"));
   ce.mark(4, st);
   const moe_status r = hip_status(launch_expert_ffn(s, L, *w, x, offsets, W.perm_token, W.perm_w,

@@ -92,7 +92,7 @@ struct GemmParams {
   int split_max;              // K ranges a tail tile may be cut into (1: none)
   int kunit;                  // K steps of BK per unit of the schedule
   int slots;                  // workgroups one XCD runs at once
-  int group_m, group_n;       // operand block of the tile order (row x weight tiles)
+  int group_n;                // weight tiles per expert-aligned block of the tile order
   int krot;                   // rotate each workgroup's K order (spreads L2 channels)
   int cache_aux;              // cache-policy bits of the operand loads
 };
@@ -175,72 +175,64 @@ struct TileMap {
   bool shared_e;
 };
 
-// The workgroup's unit of the tile schedule (tile_sched.h), then the
-// row-tile slot -> (expert, first row) map, both read from the device-side
-// offsets.  Returns false when the workgroup has no unit.  Must be called by
-// all threads of the workgroup.
+// The workgroup's unit of the tile schedule (tile_sched.h): the segments'
+// row tiles are counted and scanned from the device-side offsets into an LDS
+// prefix array, which the expert-aligned tile map then searches.  Returns
+// false when the workgroup has no unit.  Must be called by all threads of
+// the workgroup.
+constexpr int kMaxSegments = 1025;  // routed experts (at most 1024) + shared
 template <int MODE, int BM>
 __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   __shared__ int s_scan[4];
-  __shared__ int s_info[4];
+  __shared__ int s_pre[kMaxSegments + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // row tiles per segment (routed experts, then the shared expert), scanned
   const int nseg = p.E + (p.has_shared ? 1 : 0);
   const int per = (nseg + 255) / 256;
   const int e_lo = tid * per;
+  auto seg_tiles = [&](int e) {
+    const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
+    return (int)((rows + BM - 1) / BM);
+  };
   int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = e_lo + i;
-    if (e < nseg) {
-      const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
-      local += (int)((rows + BM - 1) / BM);
-    }
-  }
+  for (int i = 0; i < per; ++i)
+    if (e_lo + i < nseg) local += seg_tiles(e_lo + i);
   const int incl = wave_incl_scan(local, lane);
   if (lane == 63) s_scan[wave] = incl;
   __syncthreads();
   int before = 0;
   for (int w2 = 0; w2 < wave; ++w2) before += s_scan[w2];
-  const int Mreal = __builtin_amdgcn_readfirstlane(s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3]);
+  int run = before + incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int e = e_lo + i;
+    if (e < nseg) {
+      s_pre[e] = run;
+      run += seg_tiles(e);
+    }
+  }
+  if (tid == 0) s_pre[nseg] = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+  __syncthreads();
+  const int Mreal = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
 
   // (uniform values: pin them to scalar registers so the buffer resources and
   // offsets built from them need no per-lane loops)
   SchedUnit u{};
   const int kunits = p.K / BK / p.kunit;
-  if (!sched_unit(Mreal, p.nt, p.group_m, p.group_n, kunits, p.slots, p.split_max,
-                  (int)(blockIdx.x % kNumXcd),
-                  (int64_t)(blockIdx.x / kNumXcd), u))
+  if (!sched_unit((int64_t)Mreal * p.nt, kunits, p.slots, p.split_max,
+                  (int)(blockIdx.x % kNumXcd), (int64_t)(blockIdx.x / kNumXcd), u))
     return false;
-  const int mslot = __builtin_amdgcn_readfirstlane(u.mslot);
-  t.ntile = __builtin_amdgcn_readfirstlane(u.ntile);
+  int seg = 0, mslot = 0, ntile = 0;
+  sched_tile_of(u.q, s_pre, nseg, p.nt, p.group_n, seg, mslot, ntile);
+  t.e = __builtin_amdgcn_readfirstlane(seg);
+  t.ntile = __builtin_amdgcn_readfirstlane(ntile);
+  t.m0 = __builtin_amdgcn_readfirstlane((mslot - s_pre[seg]) * BM);
   t.kbeg = __builtin_amdgcn_readfirstlane(u.kbeg * p.kunit);
   t.nk = __builtin_amdgcn_readfirstlane(u.nk * p.kunit);
-
-  int excl = before + incl - local;
-  if (mslot >= excl && mslot < excl + local) {
-    for (int i = 0; i < per; ++i) {
-      const int e = e_lo + i;
-      if (e >= nseg) break;
-      const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
-      const int nt = (int)((rows + BM - 1) / BM);
-      if (mslot < excl + nt) {
-        s_info[0] = e;
-        s_info[1] = (mslot - excl) * BM;
-        s_info[2] = (int)rows;
-        s_info[3] = (e < p.E) ? p.offsets[e] : 0;
-        break;
-      }
-      excl += nt;
-    }
-  }
-  __syncthreads();
-  // The LDS values are the same in every lane.
-  t.e = __builtin_amdgcn_readfirstlane(s_info[0]);
-  t.m0 = __builtin_amdgcn_readfirstlane(s_info[1]);
-  t.rows = __builtin_amdgcn_readfirstlane(s_info[2]);
-  t.seg = __builtin_amdgcn_readfirstlane(s_info[3]);
   t.shared_e = (t.e == p.E);
+  t.rows = __builtin_amdgcn_readfirstlane(t.shared_e ? (int)p.T
+                                                     : p.offsets[t.e + 1] - p.offsets[t.e]);
+  t.seg = __builtin_amdgcn_readfirstlane(t.shared_e ? 0 : p.offsets[t.e]);
   return true;
 }
 
@@ -321,7 +313,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
               wgt = p.perm_w[t.seg + m];
             }
           } else {
-            orow = (int64_t)t.seg + m;
+            orow = t.shared_e ? p.P_max + m : (int64_t)t.seg + m;
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -929,7 +921,7 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GemmParams p) {
         for (int r = 0; r < 4; ++r) atomicAdd(&p.y[orow * N + nf + r], wgt * acc0[g][r]);
       } else {
         float4 v = make_float4(acc0[g][0] * sc0, acc0[g][1] * sc0, acc0[g][2] * sc0, acc0[g][3] * sc0);
-        *(float4*)(p.y_perm + ((int64_t)seg + m) * N + nf) = v;
+        *(float4*)(p.y_perm + ((shared_e ? p.P_max : (int64_t)seg) + m) * N + nf) = v;
       }
     }
   }
@@ -967,21 +959,45 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
   }
 }
 
+// Combine: y[t] = sum over kept j (in slot order) of topk_w[t, j] *
+// y_perm[slot_pos[t, j]], then + y_shared[t] (weight 1) when there is a
+// shared expert.  One thread per 4 consecutive outputs when d % 4 == 0.
+template <int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const float* __restrict__ y_shared,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w,
                                                       float* __restrict__ y, int64_t T, int k,
                                                       int d) {
-  const int64_t n = T * d;
+  const int dv = d / V;
+  const int64_t n = T * dv;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t t = i / d;
-    const int c = (int)(i % d);
-    float acc = 0.f;
+    const int64_t t = i / dv;
+    const int c = (int)(i - t * dv) * V;
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
     for (int j = 0; j < k; ++j) {
       const int32_t pos = slot_pos[t * k + j];
-      if (pos >= 0) acc += topk_w[t * k + j] * y_perm[(int64_t)pos * d + c];
+      if (pos < 0) continue;
+      const float w = topk_w[t * k + j];
+      const float* src = y_perm + (int64_t)pos * d + c;
+      if constexpr (V == 4) {
+        const float4 v4 = *(const float4*)src;
+        acc[0] += w * v4.x; acc[1] += w * v4.y; acc[2] += w * v4.z; acc[3] += w * v4.w;
+      } else {
+        acc[0] += w * src[0];
+      }
     }
-    y[i] = acc;
+    if (y_shared) {
+      const float* src = y_shared + t * d + c;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += src[v];
+    }
+    if constexpr (V == 4)
+      *(float4*)(y + t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else
+      y[t * d + c] = acc[0];
   }
 }
 
@@ -1138,16 +1154,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
     const char* ax = getenv("MOE_GEMM_AUX");
     g.krot = kr ? atoi(kr) : 0;
     g.cache_aux = ax ? atoi(ax) : 1;
-    const char* gr = getenv("MOE_GEMM_GROUP");  // "MxN" (tuning)
-    g.group_m = 8;
-    g.group_n = 4;
-    if (gr) {
-      int gm = 0, gn = 0;
-      if (sscanf(gr, "%dx%d", &gm, &gn) == 2 && gm > 0 && gn > 0) {
-        g.group_m = gm;
-        g.group_n = gn;
-      }
-    }
+    const char* gr = getenv("MOE_GEMM_GROUP");  // weight tiles per block (tuning)
+    g.group_n = gr && atoi(gr) > 0 ? atoi(gr) : 8;
   }
 
   // gate / up
@@ -1219,11 +1227,17 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
                     : launch_gemm_dt<MODE_DOWN_PERM, 128>(g2, fp8, st);
 }
 
-hipError_t launch_combine(const moe_shape& s, const float* y_perm, const int32_t* slot_pos,
-                          const float* topk_w, float* y, hipStream_t st) {
-  const int64_t n = s.T * s.d;
-  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 8192));
-  combine_kernel<<<blocks, 256, 0, st>>>(y_perm, slot_pos, topk_w, y, s.T, s.top_k, s.d);
+hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm,
+                          const int32_t* slot_pos, const float* topk_w, float* y,
+                          hipStream_t st) {
+  const float* y_shared = s.has_shared ? y_perm + P_max * (int64_t)s.d : nullptr;
+  const int V = (s.d % 4 == 0) ? 4 : 1;
+  const int64_t n = s.T * (int64_t)(s.d / V);
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 16384));
+  if (V == 4)
+    combine_kernel<4><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d);
+  else
+    combine_kernel<1><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d);
   return hipGetLastError();
 }
 

@@ -40,10 +40,17 @@ struct WsLayout {
   size_t off_perm_w;     // fp32  [P_max]
   size_t off_slot_pos;   // int32 [T*k]
   size_t off_H;          // bf16  [H_rows, d_ff]
+  bool grouped_combine;  // moe_forward: grouped output + combine instead of atomics
+  size_t off_Yp;         // fp32  [H_rows, d] (grouped_combine only)
   size_t total;
 };
 
 WsLayout ws_layout(const moe_shape& s);
+
+// Whether moe_forward combines through a grouped fp32 output and a combine
+// kernel (deterministic, no read-modify-write of y) rather than atomics in
+// the down projection: yes unless experts average 32 rows or fewer.
+bool use_grouped_combine(const moe_shape& s);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All are asynchronous.
@@ -72,7 +79,9 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L,
                              const float* perm_w, float* y_perm, float* y,
                              void* H, hipStream_t st, hipEvent_t ev_mid = nullptr);
 
-hipError_t launch_combine(const moe_shape& s, const float* y_perm,
+// y_perm holds P_max grouped rows, then (with a shared expert) T rows of
+// the shared expert's output.
+hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm,
                           const int32_t* slot_pos, const float* topk_w, float* y,
                           hipStream_t st);
 

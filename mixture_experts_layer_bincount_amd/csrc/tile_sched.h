@@ -7,8 +7,11 @@
 //
 //  * Real tiles are numbered densely, q = 0 .. R-1 with R = Mreal * nt
 //    (Mreal row tiles summed over the expert segments, nt weight tiles), in
-//    blocks of gm row tiles x gn weight tiles, row tiles fastest, so that
-//    consecutive q share both operands.
+//    expert-aligned blocks: the weight tiles are taken in groups of gn, and
+//    inside a group segment by segment, all row tiles of the segment
+//    (fastest) times the group's weight tiles.  Consecutive q then share the
+//    segment's weight panels and its activation rows; a block never mixes two
+//    experts' weights.
 //  * Workgroup ids are dealt round-robin to the XCDs; XCD x takes the
 //    contiguous q range [R x / X, R (x+1) / X), so every XCD gets the same
 //    number of tiles (+-1) and its concurrent workgroups stay inside one or
@@ -30,25 +33,33 @@ namespace moe {
 constexpr int kNumXcd = 8;  // XCDs of an MI355X; workgroups are dealt round-robin
 
 struct SchedUnit {
-  int mslot;  // row tile, 0 .. Mreal-1 (in segment order)
-  int ntile;  // weight tile, 0 .. nt-1
+  int64_t q;  // tile, 0 .. R-1
   int kbeg;   // first K unit
   int nk;     // K units
 };
 
-// Tile q -> (row tile, weight tile) in the blocked order described above,
-// with blocks of gm row tiles x gn weight tiles.
-constexpr void sched_tile_of(int64_t q, int Mreal, int nt, int gm, int gn, int& mslot,
-                             int& ntile) {
-  const int64_t col = (int64_t)Mreal * gn;  // tiles per full block column
+// Tile q -> (segment, row tile, weight tile) in the expert-aligned order
+// described above.  pre[s] is the first row tile of segment s (exclusive
+// prefix sum of the segments' row tiles, pre[nseg] = Mreal); empty segments
+// are allowed.
+constexpr void sched_tile_of(int64_t q, const int* pre, int nseg, int nt, int gn, int& seg,
+                             int& mslot, int& ntile) {
+  const int Mreal = pre[nseg];
+  const int64_t col = (int64_t)Mreal * gn;  // tiles per full weight-tile group
   const int ng = (int)(q / col);
   const int64_t r = q - (int64_t)ng * col;
   const int nh = (nt - ng * gn) < gn ? (nt - ng * gn) : gn;
-  const int mg = (int)(r / ((int64_t)gm * nh));
-  const int r2 = (int)(r - (int64_t)mg * gm * nh);
-  const int mh = (Mreal - mg * gm) < gm ? (Mreal - mg * gm) : gm;
-  mslot = mg * gm + r2 % mh;
-  ntile = ng * gn + r2 / mh;
+  // the last segment s with pre[s] * nh <= r (it is never empty)
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)pre[mid] * nh <= r) lo = mid; else hi = mid - 1;
+  }
+  seg = lo;
+  const int me = pre[seg + 1] - pre[seg];
+  const int64_t loc = r - (int64_t)pre[seg] * nh;
+  mslot = pre[seg] + (int)(loc % me);
+  ntile = ng * gn + (int)(loc / me);
 }
 
 // The K-range split of the tail round: pieces per tile for `rem` tiles on
@@ -74,27 +85,24 @@ constexpr int64_t sched_units_bound(int64_t R_max, int slots) {
   return (R_max + kNumXcd - 1) / kNumXcd + slots;
 }
 
-// Unit of workgroup `i` of XCD `xcd`.  kunits: K units of a whole tile.
-// Returns false when the workgroup has nothing to do.
-constexpr bool sched_unit(int Mreal, int nt, int gm, int gn, int kunits, int slots,
-                          int split_max, int xcd, int64_t i, SchedUnit& u) {
-  const int64_t R = (int64_t)Mreal * nt;
+// Unit of workgroup `i` of XCD `xcd` among R tiles.  kunits: K units of a
+// whole tile.  Returns false when the workgroup has nothing to do.
+constexpr bool sched_unit(int64_t R, int kunits, int slots, int split_max, int xcd, int64_t i,
+                          SchedUnit& u) {
   const int64_t q0 = R * xcd / kNumXcd, q1 = R * (xcd + 1) / kNumXcd;
   const int64_t n = q1 - q0;
   const int64_t full = n / slots * slots;
-  int64_t q = 0;
   int piece = 0, S = 1;
   if (i < full) {
-    q = q0 + i;
+    u.q = q0 + i;
   } else {
     const int rem = (int)(n - full);
     S = sched_tail_split(rem, slots, split_max);
     const int64_t j = i - full;
     if (j >= (int64_t)rem * S) return false;
-    q = q0 + full + j / S;
+    u.q = q0 + full + j / S;
     piece = (int)(j % S);
   }
-  sched_tile_of(q, Mreal, nt, gm, gn, u.mslot, u.ntile);
   u.kbeg = (int)((int64_t)kunits * piece / S);
   u.nk = (int)((int64_t)kunits * (piece + 1) / S) - u.kbeg;
   return true;

@@ -1,45 +1,53 @@
 // Host check of the grouped-GEMM tile schedule (csrc/tile_sched.h): for many
-// shapes, the units of all workgroups cover every (row tile, weight tile)
-// exactly once and, per tile, partition its K units into disjoint ranges;
-// no XCD has more units than the grid provides; tail splits stay within
-// split_max and the concurrent slots.  Prints "ok <cases>" or the first
-// failure, and exits non-zero on failure.
+// shapes and per-segment row-tile counts (empty segments included), the units
+// of all workgroups cover every (row tile, weight tile) exactly once and, per
+// tile, partition its K units into disjoint ranges; every row tile maps to
+// the segment that owns it; no XCD has more units than the grid provides;
+// tail pieces are no shorter than split_max allows.  Prints "ok <cases>" or
+// the first failure, and exits non-zero on failure.
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <random>
 #include <vector>
 
 #include "tile_sched.h"
 
 using namespace moe;
 
-static int check(int Mreal, int nt, int gm, int gn, int kunits, int slots, int split_max) {
+static int check(const std::vector<int>& tiles_per_seg, int nt, int gn, int kunits, int slots,
+                 int split_max) {
+  const int nseg = (int)tiles_per_seg.size();
+  std::vector<int> pre(nseg + 1, 0);
+  for (int s = 0; s < nseg; ++s) pre[s + 1] = pre[s] + tiles_per_seg[s];
+  const int Mreal = pre[nseg];
   const int64_t R = (int64_t)Mreal * nt;
   std::vector<int> cover((size_t)R * kunits, 0);
+  std::vector<int> tile_seen((size_t)R, 0);
   const int64_t per_xcd = sched_units_bound(R, slots);
   for (int x = 0; x < kNumXcd; ++x) {
     int64_t units = 0;
     for (int64_t i = 0; i < per_xcd + 3; ++i) {
       SchedUnit u{};
-      const bool ok = sched_unit(Mreal, nt, gm, gn, kunits, slots, split_max, x, i, u);
-      if (!ok) continue;
+      if (!sched_unit(R, kunits, slots, split_max, x, i, u)) continue;
       if (i >= per_xcd) {
         printf("FAIL unit beyond grid M=%d nt=%d x=%d i=%lld\n", Mreal, nt, x, (long long)i);
         return 1;
       }
       ++units;
-      if (u.mslot < 0 || u.mslot >= Mreal || u.ntile < 0 || u.ntile >= nt || u.nk <= 0 ||
-          u.kbeg < 0 || u.kbeg + u.nk > kunits) {
-        printf("FAIL bad unit M=%d nt=%d x=%d i=%lld -> %d %d %d %d\n", Mreal, nt, x,
-               (long long)i, u.mslot, u.ntile, u.kbeg, u.nk);
+      int seg = -1, m = -1, n = -1;
+      sched_tile_of(u.q, pre.data(), nseg, nt, gn, seg, m, n);
+      if (u.q < 0 || u.q >= R || seg < 0 || seg >= nseg || m < pre[seg] || m >= pre[seg + 1] ||
+          n < 0 || n >= nt || u.nk <= 0 || u.kbeg < 0 || u.kbeg + u.nk > kunits) {
+        printf("FAIL bad unit M=%d nt=%d gn=%d x=%d i=%lld -> q=%lld seg=%d m=%d n=%d k=%d+%d\n",
+               Mreal, nt, gn, x, (long long)i, (long long)u.q, seg, m, n, u.kbeg, u.nk);
         return 1;
       }
       if (u.nk < kunits / split_max) {
-        printf("FAIL split beyond split_max M=%d nt=%d\n", Mreal, nt);
+        printf("FAIL piece shorter than split_max allows M=%d nt=%d\n", Mreal, nt);
         return 1;
       }
-      for (int k = u.kbeg; k < u.kbeg + u.nk; ++k)
-        cover[((size_t)u.mslot * nt + u.ntile) * kunits + k]++;
+      for (int k = u.kbeg; k < u.kbeg + u.nk; ++k) cover[((size_t)m * nt + n) * kunits + k]++;
     }
     if (units != sched_units_of_xcd(R, x, slots, split_max)) {
       printf("FAIL unit count M=%d nt=%d x=%d\n", Mreal, nt, x);
@@ -48,8 +56,19 @@ static int check(int Mreal, int nt, int gm, int gn, int kunits, int slots, int s
   }
   for (size_t c = 0; c < cover.size(); ++c)
     if (cover[c] != 1) {
-      printf("FAIL cover M=%d nt=%d kunits=%d slots=%d split=%d at %zu: %d\n", Mreal, nt,
-             kunits, slots, split_max, c, cover[c]);
+      printf("FAIL cover M=%d nt=%d gn=%d kunits=%d slots=%d split=%d at %zu: %d\n", Mreal, nt,
+             gn, kunits, slots, split_max, c, cover[c]);
+      return 1;
+    }
+  // the tile map alone is a bijection q <-> (row tile, weight tile)
+  for (int64_t q = 0; q < R; ++q) {
+    int seg = -1, m = -1, n = -1;
+    sched_tile_of(q, pre.data(), nseg, nt, gn, seg, m, n);
+    tile_seen[(size_t)m * nt + n]++;
+  }
+  for (size_t c = 0; c < tile_seen.size(); ++c)
+    if (tile_seen[c] != 1) {
+      printf("FAIL tile map not a bijection M=%d nt=%d gn=%d\n", Mreal, nt, gn);
       return 1;
     }
   return 0;
@@ -57,28 +76,41 @@ static int check(int Mreal, int nt, int gm, int gn, int kunits, int slots, int s
 
 int main() {
   int cases = 0;
-  const int Ms[] = {1, 2, 3, 7, 8, 9, 15, 16, 17, 33, 35, 40, 67, 131, 256, 370};
-  const int nts[] = {1, 2, 3, 4, 5, 7, 8, 16, 17, 56, 112};
-  const int kus[] = {1, 4, 7, 64, 224};
-  const int slotss[] = {1, 3, 32, 64};
+  std::mt19937 rng(12345);
+  const int nsegs[] = {1, 2, 3, 8, 9, 65, 257};
+  const int nts[] = {1, 3, 4, 7, 8, 16, 17, 56};
+  const int kus[] = {1, 7, 64, 224};
+  const int slotss[] = {1, 3, 32};
   const int splits[] = {1, 2, 56};
-  for (int M : Ms)
-    for (int nt : nts)
-      for (int ku : kus)
-        for (int sl : slotss)
-          for (int sp : splits)
-            for (int g = 0; g < 3; ++g) {
-              const int gm = g == 0 ? 8 : g == 1 ? 4 : 1, gn = g == 0 ? 4 : g == 1 ? 8 : 16;
-              if (check(M, nt, gm, gn, ku, sl, sp < ku ? sp : ku)) return 1;
-              ++cases;
-            }
-  // the blocked order: consecutive tiles of a full block share row tiles
-  // within groups of 8 and weight tiles within groups of 4
+  const int gns[] = {1, 4, 8, 16};
+  for (int nseg : nsegs)
+    for (int shape = 0; shape < 3; ++shape) {
+      // row tiles per segment: uniform small, skewed with empty segments, all 1
+      std::vector<int> tps(nseg);
+      for (int s = 0; s < nseg; ++s) {
+        if (shape == 0) tps[s] = 1 + (int)(rng() % 5);
+        else if (shape == 1) tps[s] = (rng() % 3 == 0) ? 0 : (int)(rng() % 4);
+        else tps[s] = 1;
+      }
+      if (shape == 1) tps[0] = 3;  // at least one tile
+      for (int nt : nts)
+        for (int gn : gns)
+          for (int ku : kus)
+            for (int sl : slotss)
+              for (int sp : splits) {
+                if (nseg * nt > 4000 && (ku > 7 || sl != 32)) continue;  // keep it quick
+                if (check(tps, nt, gn, ku, sl, sp < ku ? sp : ku)) return 1;
+                ++cases;
+              }
+    }
+  // expert-aligned blocks: with segments of 4 row tiles and gn = 8, the first
+  // 32 tiles are segment 0's 4 row tiles x weight tiles 0..7
+  std::vector<int> pre = {0, 4, 8, 12};
   for (int64_t q = 0; q < 32; ++q) {
-    int m = 0, n = 0;
-    sched_tile_of(q, 40, 112, 8, 4, m, n);
-    if (m != (int)(q % 8) || n != (int)(q / 8)) {
-      printf("FAIL block order q=%lld -> %d %d\n", (long long)q, m, n);
+    int seg = -1, m = -1, n = -1;
+    sched_tile_of(q, pre.data(), 3, 112, 8, seg, m, n);
+    if (seg != 0 || m != (int)(q % 4) || n != (int)(q / 4)) {
+      printf("FAIL block order q=%lld -> seg %d m %d n %d\n", (long long)q, seg, m, n);
       return 1;
     }
   }

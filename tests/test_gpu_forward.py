@@ -63,12 +63,14 @@ def test_tiny_page_layer(moe):
     print(f"[tiny] err={rep['err']:.3e} load={out['counts'].tolist()}", flush=True)
 
 
-@pytest.mark.parametrize("T,seed", [(600, 5), (64, 6)])
-def test_unfused_path_matches_fused(moe, T, seed):
+@pytest.mark.parametrize("T,seed,shared", [(600, 5, False), (64, 6, False), (200, 7, True)])
+def test_unfused_path_matches_fused(moe, monkeypatch, T, seed, shared):
     """moe_expert_ffn into a grouped output, then moe_combine, against the
     fused scatter-add path and the oracle (600 tokens: tiled GEMMs; 64:
-    the weight-streaming kernels)."""
-    cfg = custom_config(T, 256, 8, 2, 256, cf=1.0, seed=seed)
+    the weight-streaming kernels; 200 with a shared expert, whose rows follow
+    the grouped rows)."""
+    monkeypatch.setenv("MOE_COMBINE", "atomic")
+    cfg = custom_config(T, 256, 8, 2, 256, cf=1.0, seed=seed, shared=shared)
     wl = Workload(cfg)
     out, layer, dev = gpu_forward(wl)
     s = layer.shape
@@ -84,7 +86,7 @@ def test_unfused_path_matches_fused(moe, T, seed):
     slot_pos = torch.empty(A, dtype=torch.int32, device="cuda")
     moe.moe_dispatch(s, layer.topk_idx, layer.topk_w, None, counts, offsets, None, perm_token,
                      perm_w, slot_pos, None, ws)
-    y_perm = torch.empty((P_max, d), dtype=torch.float32, device="cuda")
+    y_perm = torch.empty((P_max + (T if shared else 0), d), dtype=torch.float32, device="cuda")
     moe.moe_expert_ffn(s, layer.weights, dev["x"], offsets, perm_token, None, y_perm, None, ws)
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
     moe.moe_combine(s, y_perm, slot_pos, layer.topk_w, y)
@@ -96,6 +98,32 @@ def test_unfused_path_matches_fused(moe, T, seed):
     out2 = dict(out)
     out2["y"] = y_un
     check_forward(wl, out2)
+
+
+@pytest.mark.parametrize("form", ["atomic", "grouped"])
+def test_combine_forms(moe, monkeypatch, form):
+    """Both combine forms of moe_forward against the oracle: fp32 atomic adds
+    in the down projection (the default at decode sizes), and a grouped
+    output summed by the combine pass, on a shape with k = 4, a shared expert
+    and a capacity limit."""
+    monkeypatch.setenv("MOE_COMBINE", form)
+    cfg = custom_config(400, 256, 16, 4, 256, shared=True, cf=1.25, seed=41)
+    wl = Workload(cfg)
+    out, _, _ = gpu_forward(wl)
+    rep = check_forward(wl, out)
+    print(f"[combine {form}] err={rep['err']:.3e}", flush=True)
+
+
+def test_grouped_combine_is_deterministic(moe, monkeypatch):
+    """The grouped-output combine sums in slot order: two runs are bit-equal
+    even with k = 8 and a shared expert."""
+    monkeypatch.setenv("MOE_COMBINE", "grouped")
+    cfg = custom_config(300, 256, 32, 8, 128, shared=True, seed=43)
+    wl = Workload(cfg)
+    out1, layer, dev = gpu_forward(wl)
+    layer(dev["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.y.cpu().numpy(), out1["y"])
 
 
 def test_T0_is_a_noop(moe):

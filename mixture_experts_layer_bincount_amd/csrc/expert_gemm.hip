@@ -246,9 +246,11 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
 
 // Epilogue.  32x32 accumulator register r of lane l is row (r/4)*8 +
 // (l/32)*4 + r%4, column l%32 of the 32x32 tile.  arow0: the wave's first
-// activation row in the tile; brow: its four 32-row weight tiles; n0: first
-// output column of the tile; wn: the wave's column group.
-template <int MODE, bool FP8>
+// activation row in the tile, its i-th 32-row granule starting RS rows
+// further per i (32: contiguous rows, 64: granules interleaved with the other
+// row wave); brow: its four 32-row weight tiles; n0: first output column of
+// the tile; wn: the wave's column group.
+template <int MODE, bool FP8, int RS>
 __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
                                            const TileMap& t, int arow0, int n0, int wn,
                                            const int (&brow)[4]) {
@@ -258,12 +260,12 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
   const int N = p.N;
   if (MODE == MODE_GATEUP) {
     // transposed product: acc[i][j] holds weight row brow[j] + R, activation
-    // row arow0 + i*32 + ccol; tiles j and j + 2 are the gate and up halves.
+    // row arow0 + i*RS + ccol; tiles j and j + 2 are the gate and up halves.
     const int64_t hbase = t.shared_e ? p.P_max : (int64_t)t.seg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
-      const int m = t.m0 + arow0 + i * 32 + ccol;
+      const int m = t.m0 + arow0 + i * RS + ccol;
       if (m >= t.rows) continue;
       uint16_t* hrow = p.H + (hbase + m) * N;
 #pragma unroll
@@ -293,7 +295,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
       }
     }
   } else {
-    // acc[i][j]: activation row arow0 + i*32 + R, output column brow[j] + ccol.
+    // acc[i][j]: activation row arow0 + i*RS + R, output column brow[j] + ccol.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -301,7 +303,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
         __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = t.m0 + arow0 + i * 32 + q * 8 + rbase + r;
+          const int m = t.m0 + arow0 + i * RS + q * 8 + rbase + r;
           if (m >= t.rows) continue;
           float wgt = 1.f;
           int64_t orow;
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   }
 #undef MOE_LOAD_STAGE
 #undef MOE_STORE_STAGE
-  store_tile<MODE, FP8>(p, acc, t, arow0, n0, wn, brow);
+  store_tile<MODE, FP8, 32>(p, acc, t, arow0, n0, wn, brow);
 }
 
 // ---------------------------------------------------------------------------
@@ -563,7 +565,7 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX, bool IL>
+template <int MODE, int KB, int NS, int MOE_AUX>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   using C = DmaCfg<KB, NS>;
   constexpr int BNB = 256;
@@ -630,70 +632,34 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     }
   };
 
+  // Wave (wm, wn) owns the 32-row granules wm, wm + 2, wm + 4, wm + 6 of the
+  // tile (interleaved, so a partial tile's valid granules split evenly over
+  // the two row waves) and 128 weight rows.  Only the granules that hold rows
+  // of the segment are computed: a wave runs the main loop compiled for its
+  // count NG (0..4) of valid granules; every wave still takes part in the DMA
+  // and the barriers.
   const int wm = wave >> 1, wn = wave & 1;
-  const int arow0 = wm * 128;
+  const int arow0 = wm * 32;
   int brow[4];
   wave_brows<MODE, BNB>(wn, brow);
   f32x16 acc[4][4];
   zero_acc(acc);
+  const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
+  const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
 
   // fragment reads: tile rows are 32-aligned, so swz(row) = (frow / RPS) % CPR
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
   const int swz = (frow / C::RPS) % C::CPR;
-  auto compute = [&](int stage) __attribute__((always_inline)) {
-    const char* a = dlds + stage * C::STAGE_BYTES;
-    const char* b = a + C::TILE_BYTES;
-    // one 32-deep half at a time: 16 fragment reads in flight, then 32 MFMAs
-    static_for<KB / 32>([&](auto h) {
-      bf16x8 af[2][4], bfr[2][4];
-      static_for<2>([&](auto kk) {
-        const int c = (h * 4 + kk * 2 + fhalf) ^ swz;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[kk][i] = *(const bf16x8*)(a + (arow0 + i * 32 + frow) * C::RB + c * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + c * 16);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_slice<MODE>(acc, af[0], bfr[0]);
-      mfma_slice<MODE>(acc, af[1], bfr[1]);
-    });
-  };
 
-  if constexpr (!IL) {
-  // ---- pipeline.  Before computing step kt a wave waits until its own DMA
-  // for step kt has landed (the DMA of the following steps already issued
-  // may still be in flight), then a barrier makes every wave's part visible
-  // and frees the stage computed at kt - 1, which is refilled with step
-  // kt + NS - 1.  (A bare s_barrier: the fence of __syncthreads would wait
-  // for all DMA.)
-  if (nk > 0) {
-    static_for<NS - 1>([&](auto s) {
-      if (s < nk) issue(s, s);
-    });
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(nk - 1 - kt, NS - 2);  // later steps already issued
-      if (ahead >= 2)
-        wait_vmcnt<2 * C::NI>();
-      else if (ahead == 1)
-        wait_vmcnt<C::NI>();
-      else
-        wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-      compute(kt % NS);
-    }
-  }
-  } else {
-  // ---- interleaved pipeline over 32-deep K slices (HPS per DMA step).  The
-  // fragments of slice s + 1 are read from LDS while the MFMAs of slice s run
-  // (two fragment buffers, one read between every two MFMAs).  Before the
+  // ---- pipeline over 32-deep K slices (HPS per DMA step).  The fragments of
+  // slice s + 1 are read from LDS while the MFMAs of slice s run (two
+  // fragment buffers, LDS reads interleaved with the MFMAs).  Before the
   // first read of a new step t, each wave has finished its reads of step
   // t - 1 (lgkmcnt 0) and waited for its own DMA of step t; one barrier then
   // makes step t visible to all waves and frees the stage of step t - 1, which
-  // is refilled with step t + NS - 1.
+  // is refilled with step t + NS - 1.  (A bare s_barrier: the fence of
+  // __syncthreads would wait for all DMA.)
   constexpr int HPS = KB / 32;
   const int nsl = nk * HPS;
   // per-lane LDS byte offsets of the fragment rows (stage 0, chunk slot 0)
@@ -703,20 +669,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   static_for<HPS>([&](auto h) {
     static_for<2>([&](auto kk) { col_off[h][kk] = (((h * 4 + kk * 2 + fhalf) ^ swz) * 16); });
   });
-  bf16x8 fa0[2][4], fb0[2][4], fa1[2][4], fb1[2][4];
-  auto read_slice = [&](int sl, bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4]) __attribute__((always_inline)) {
-    const int stage = (sl / HPS) % NS;
-    const int h = sl % HPS;
-    const char* a = dlds + stage * C::STAGE_BYTES;
-    const char* b = a + C::TILE_BYTES;
-    static_for<2>([&](auto kk) {
-      const int co = (HPS == 1 || h == 0) ? col_off[0][kk] : col_off[HPS - 1][kk];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[kk][i] = *(const bf16x8*)(a + a_row_off + i * 32 * C::RB + co);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
-    });
-  };
   // step boundary before slice sl (sl % HPS == 0, sl > 0): see above
   auto step_sync = [&](int sl) __attribute__((always_inline)) {
     const int t = sl / HPS;
@@ -730,20 +682,51 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     __builtin_amdgcn_s_barrier();
     if (t + NS - 1 < nk) issue(t + NS - 1, (t + NS - 1) % NS);
   };
-  // MFMAs of one slice from (fa, fb) with the reads of slice `next` into
-  // (ga, gb) interleaved.  `next` may be past the end: it then rereads a
-  // valid stage and the values go unused.
-  auto slice = [&](bf16x8 (&fa)[2][4], bf16x8 (&fb)[2][4], int next, bf16x8 (&ga)[2][4],
-                   bf16x8 (&gb)[2][4]) __attribute__((always_inline)) {
-    read_slice(next < nsl ? next : nsl - 1, ga, gb);
-    mfma_slice<MODE>(acc, fa[0], fb[0]);
-    mfma_slice<MODE>(acc, fa[1], fb[1]);
-    static_for<16>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-    });
-  };
-  if (nk > 0) {
+  auto run = [&](auto NGc) __attribute__((always_inline)) {
+    constexpr int NG = decltype(NGc)::value;
+    constexpr int NGA = NG > 0 ? NG : 1;
+    bf16x8 fa0[2][NGA], fb0[2][4], fa1[2][NGA], fb1[2][4];
+    auto read_slice = [&](int sl, bf16x8 (&fa)[2][NGA], bf16x8 (&fb)[2][4]) __attribute__((always_inline)) {
+      if constexpr (NG > 0) {
+        const int stage = (sl / HPS) % NS;
+        const int h = sl % HPS;
+        const char* a = dlds + stage * C::STAGE_BYTES;
+        const char* b = a + C::TILE_BYTES;
+        static_for<2>([&](auto kk) {
+          const int co = (HPS == 1 || h == 0) ? col_off[0][kk] : col_off[HPS - 1][kk];
+#pragma unroll
+          for (int i = 0; i < NG; ++i)
+            fa[kk][i] = *(const bf16x8*)(a + a_row_off + i * 64 * C::RB + co);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
+        });
+      }
+    };
+    // MFMAs of one slice from (fa, fb) with the reads of slice `next` into
+    // (ga, gb) interleaved.  `next` may be past the end: it then rereads a
+    // valid stage and the values go unused.
+    auto slice = [&](bf16x8 (&fa)[2][NGA], bf16x8 (&fb)[2][4], int next, bf16x8 (&ga)[2][NGA],
+                     bf16x8 (&gb)[2][4]) __attribute__((always_inline)) {
+      if constexpr (NG > 0) {
+        read_slice(next < nsl ? next : nsl - 1, ga, gb);
+        static_for<2>([&](auto kk) {
+#pragma unroll
+          for (int i = 0; i < NG; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (MODE == MODE_GATEUP)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+            }
+        });
+        constexpr int NR = 2 * (NG + 4), NM = 8 * NG, MPR = (NM + NR - 1) / NR;
+        static_for<NR>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);  // MFMAs
+        });
+      }
+    };
     static_for<NS - 1>([&](auto s) {
       if (s < nk) issue(s, s);
     });
@@ -765,9 +748,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       slice(fa1, fb1, sl + 2, fa0, fb0);
     }
     if (sl < nsl) slice(fa0, fb0, nsl, fa1, fb1);
+  };
+  if (nk > 0) {
+    if (ng >= 4)
+      run(std::integral_constant<int, 4>{});
+    else if (ng == 3)
+      run(std::integral_constant<int, 3>{});
+    else if (ng == 2)
+      run(std::integral_constant<int, 2>{});
+    else if (ng == 1)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, 0>{});
   }
-  }
-  store_tile<MODE, false>(p, acc, t, arow0, n0, wn, brow);
+  store_tile<MODE, false, 64>(p, acc, t, arow0, n0, wn, brow);
 }
 
 // ---------------------------------------------------------------------------
@@ -1036,9 +1030,12 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE, int KB, int NS, bool IL>
-hipError_t launch_gemm_dma_cfg(const GemmParams& p0, hipStream_t st) {
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, IL>;
+// The LDS-DMA kernel: 64-deep K steps in two stages.
+template <int MODE>
+hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
+  if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
+  constexpr int KB = 64, NS = 2;
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1>;
   static int slots = 0;
   if (!slots) {
     hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1049,33 +1046,20 @@ hipError_t launch_gemm_dma_cfg(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
-  grouped_gemm_dma_kernel<MODE, KB, NS, 1, IL><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
   return hipGetLastError();
 }
 
-// DMA pipeline shape: 64-deep steps in two stages, or 32-deep steps in four
-// (MOE_GEMM_DMA_CFG=32x4, and always when K is not a multiple of 64);
-// the interleaved fragment pipeline unless MOE_GEMM_IL=0.
-template <int MODE>
-hipError_t launch_gemm_dma(const GemmParams& p, hipStream_t st) {
-  if (p.mt_max <= 0 || p.nt <= 0) return hipSuccess;
-  const char* v = getenv("MOE_GEMM_DMA_CFG");
-  const char* il = getenv("MOE_GEMM_IL");
-  const bool IL = !(il && atoi(il) == 0);
-  const bool k64 = (p.K / BK) % 2 == 0 && !(v && !strcmp(v, "32x4"));
-  if (k64) return IL ? launch_gemm_dma_cfg<MODE, 64, 2, true>(p, st)
-                     : launch_gemm_dma_cfg<MODE, 64, 2, false>(p, st);
-  return IL ? launch_gemm_dma_cfg<MODE, 32, 4, true>(p, st)
-            : launch_gemm_dma_cfg<MODE, 32, 4, false>(p, st);
-}
-
-// bf16 weights with 256-row tiles take the LDS-DMA kernel unless
-// MOE_GEMM_DMA=0; fp8 weights the register-staged one.
+// bf16 weights with 256-row tiles and K a multiple of 64 take the LDS-DMA
+// kernel (MOE_GEMM_DMA[_GATEUP|_DOWN]=0 selects the register-staged one, for
+// comparison); fp8 weights the register-staged one.
 template <int MODE, int BM>
 hipError_t launch_gemm_dt(const GemmParams& p, bool fp8, hipStream_t st) {
   if (fp8) return launch_gemm<MODE, true, BM>(p, st);
-  const char* v = getenv("MOE_GEMM_DMA");
-  if (BM == DMA_BM && !(v && atoi(v) == 0)) return launch_gemm_dma<MODE>(p, st);
+  const char* v = getenv(MODE == MODE_GATEUP ? "MOE_GEMM_DMA_GATEUP" : "MOE_GEMM_DMA_DOWN");
+  if (!v) v = getenv("MOE_GEMM_DMA");
+  if (BM == DMA_BM && (p.K / BK) % 2 == 0 && !(v && atoi(v) == 0))
+    return launch_gemm_dma<MODE>(p, st);
   return launch_gemm<MODE, false, BM>(p, st);
 }
 

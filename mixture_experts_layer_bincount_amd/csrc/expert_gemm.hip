@@ -538,18 +538,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
 constexpr int DMA_BM = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int KB, int NS>
+template <int KB, int NS, bool FP8>
 struct DmaCfg {
-  static constexpr int RB = KB * 2;                 // bytes per tile row and stage
-  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
-  static constexpr int RPS = 256 / RB;              // rows per 256-byte bank sweep
-  static constexpr int ROWS_PER_INST = 1024 / RB;   // rows one wave-level DMA fills
-  static constexpr int NI = 512 / ROWS_PER_INST / 4;  // DMA instructions per wave and stage
-  static constexpr int TILE_BYTES = 256 * RB;       // one operand tile (A or B)
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  // activation (A) tile: 256 rows of KB bf16
+  static constexpr int RB = KB * 2;                 // bytes per A row and stage
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per A row
+  static constexpr int RPS = 256 / RB;              // A rows per 256-byte bank sweep
+  static constexpr int ROWS_PER_INST = 1024 / RB;   // A rows one wave-level DMA fills
+  static constexpr int NI = 128 / ROWS_PER_INST;    // A DMA instructions per wave and stage
+  static constexpr int TILE_BYTES = 256 * RB;       // the A tile
+  // weight (B) tile: 256 rows of KB bf16, or KB fp8 codes
+  static constexpr int RBB = KB * (FP8 ? 1 : 2);    // bytes per B row and stage
+  static constexpr int CPRB = RBB / 16;
+  static constexpr int RPSB = 256 / RBB;
+  static constexpr int ROWS_PER_INST_B = 1024 / RBB;
+  static constexpr int NIB = 128 / ROWS_PER_INST_B; // B DMA instructions per wave and stage
+  static constexpr int B_TILE_BYTES = 256 * RBB;
+  static constexpr int STAGE_BYTES = TILE_BYTES + B_TILE_BYTES;
+  static constexpr int NI_MAX = NI > NIB ? NI : NIB;
   static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
-  static_assert(KB % 16 == 0 && NS >= 2 && NS <= 4, "DMA pipeline shape");
-  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4, "DMA pipeline shape");
+  static_assert(LDS <= 150 * 1024, "LDS budget (with the static tile-map arrays)");
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -560,14 +569,26 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// 8 OCP e4m3 codes (K order, low byte first) -> 8 bf16, exactly: the gfx950
+// scaled conversion with scale 1 (e4m3 values are all representable in bf16).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // s_waitcnt with only the LDS counter constrained: lgkmcnt(0).
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX>
+template <int MODE, int KB, int NS, int MOE_AUX, bool FP8>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  using C = DmaCfg<KB, NS>;
+  using C = DmaCfg<KB, NS, FP8>;
+  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
   constexpr int BNB = 256;
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
   TileMap t;
@@ -581,29 +602,35 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   const int nk = (t.nk * BK) / KB;
 
   // ---- DMA sources.  Waves 0, 1 fill the A tile, waves 2, 3 the B tile
-  // (in GATEUP wave 2 the W1 rows, wave 3 the W3 rows).  Wave w's instruction
-  // j fills tile rows ((w & 1) * NI + j) * ROWS_PER_INST + lane / CPR; lane
-  // i writes chunk slot i % CPR, which holds K chunk (i % CPR) ^ swz(row).
-  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A, p.A_bytes);
+  // (in GATEUP wave 2 the W1 rows, wave 3 the W3 rows).  A wave's
+  // instruction j fills 1 KiB: tile rows ((w & 1) * NI + j) * ROWS_PER_INST +
+  // lane / CPR (B: the _B / CPRB / NIB counterparts); lane i writes chunk slot
+  // i % CPR, which holds K chunk (i % CPR) ^ swz(row).
   const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
-  const int64_t ebytes = (int64_t)N * K * 2;
+  const int64_t ebytes = (int64_t)N * K * WB;
   const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
-  const __amdgpu_buffer_rsrc_t rsB0 =
-      uniform_rsrc((const char*)(t.shared_e ? p.B0s : p.B0) + eoff, ebytes);
-  __amdgpu_buffer_rsrc_t rsB1 = rsB0;
-  if (MODE == MODE_GATEUP)
-    rsB1 = uniform_rsrc((const char*)(t.shared_e ? p.B1s : p.B1) + eoff, ebytes);
-  uint32_t voff[C::NI];
-  static_for<C::NI>([&](auto j) {
-    const int r = ((wave & 1) * C::NI + j) * C::ROWS_PER_INST + lane / C::CPR;  // 0..255
-    const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
+  // the B wave's own weight matrix (GATEUP: wave 3 reads W3, wave 2 W1), as
+  // one resource built from a pointer chosen up front (a select between two
+  // resources would go through scratch memory)
+  const bool w3 = (MODE == MODE_GATEUP) && wave == 3;
+  const void* bsrc = w3 ? (t.shared_e ? p.B1s : p.B1) : (t.shared_e ? p.B0s : p.B0);
+  // each wave's one DMA source (A waves: the activations)
+  const bool a_wave = wave < 2;
+  const __amdgpu_buffer_rsrc_t rsW =
+      uniform_rsrc(a_wave ? (const char*)p.A : (const char*)bsrc + eoff, a_wave ? p.A_bytes : ebytes);
+  uint32_t voff[C::NI_MAX];
+  static_for<C::NI_MAX>([&](auto j) {
     if (wave < 2) {
-      const int m = min(t.m0 + r, t.rows - 1);
+      const int r = ((wave & 1) * C::NI + j) * C::ROWS_PER_INST + lane / C::CPR;  // 0..255
+      const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
+      const int m = min(t.m0 + min(r, 255), t.rows - 1);
       voff[j] = (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16);
     } else {
-      int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+      const int r = ((wave & 1) * C::NIB + j) * C::ROWS_PER_INST_B + lane / C::CPRB;
+      const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
+      int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + min(r, 255);
       n = min(n, N - 1);
-      voff[j] = (uint32_t)(((int64_t)n * K + kbeg_el) * 2 + chunk * 16);
+      voff[j] = (uint32_t)(((int64_t)n * K + kbeg_el) * WB + chunk * 16);
     }
   });
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
@@ -612,22 +639,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // K*2 bytes, a power of two in the common shapes).
   const int krot = p.krot ? __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)max(nk, 1))) : 0;
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    char* gbase = dlds + stage * C::STAGE_BYTES + (wave >> 1) * C::TILE_BYTES +
-                  (wave & 1) * (C::TILE_BYTES / 2);
     int kr = kt + krot;
     kr = kr >= nk ? kr - nk : kr;
-    const int soff = __builtin_amdgcn_readfirstlane(kr * C::RB);
-    if (wave < 2) {
+    char* gbase = dlds + stage * C::STAGE_BYTES +
+                  (a_wave ? (wave & 1) * (C::TILE_BYTES / 2)
+                          : C::TILE_BYTES + (wave & 1) * (C::B_TILE_BYTES / 2));
+    const int soff = __builtin_amdgcn_readfirstlane(kr * (a_wave ? C::RB : C::RBB));
+    if constexpr (C::NI == C::NIB) {
       static_for<C::NI>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
-    } else if (MODE == MODE_GATEUP && wave == 3) {
+    } else if (a_wave) {
       static_for<C::NI>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
     } else {
-      static_for<C::NI>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+      static_for<C::NIB>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
     }
   };
@@ -669,6 +697,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   static_for<HPS>([&](auto h) {
     static_for<2>([&](auto kk) { col_off[h][kk] = (((h * 4 + kk * 2 + fhalf) ^ swz) * 16); });
   });
+  // fp8 weight rows: 8 codes (8 bytes) per fragment, half of a swizzled
+  // 16-byte chunk; the B tile rows are 32-aligned as well
+  const int swzb = FP8 ? (frow / C::RPSB) % C::CPRB : 0;
   // step boundary before slice sl (sl % HPS == 0, sl > 0): see above
   auto step_sync = [&](int sl) __attribute__((always_inline)) {
     const int t = sl / HPS;
@@ -697,8 +728,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
           for (int i = 0; i < NG; ++i)
             fa[kk][i] = *(const bf16x8*)(a + a_row_off + i * 64 * C::RB + co);
+          if constexpr (!FP8) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
+            for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
+          } else {
+            const int cb = ((h * 2 + kk) ^ swzb) * 16 + fhalf * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              fb[kk][j] = fp8x8_to_bf16x8(*(const uint2*)(b + (brow[j] + frow) * C::RBB + cb));
+          }
         });
       }
     };
@@ -761,7 +799,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     else
       run(std::integral_constant<int, 0>{});
   }
-  store_tile<MODE, false, 64>(p, acc, t, arow0, n0, wn, brow);
+  store_tile<MODE, FP8, 64>(p, acc, t, arow0, n0, wn, brow);
 }
 
 // ---------------------------------------------------------------------------
@@ -1031,36 +1069,36 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
 }
 
 // The LDS-DMA kernel: 64-deep K steps in two stages.
-template <int MODE>
+template <int MODE, bool FP8>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
   constexpr int KB = 64, NS = 2;
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1>;
+  using C = DmaCfg<KB, NS, FP8>;
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8>;
   static int slots = 0;
   if (!slots) {
     hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)DmaCfg<KB, NS>::LDS);
+                                         (int)C::LDS);
     if (err != hipSuccess) return err;
-    slots = xcd_slots(kern, DmaCfg<KB, NS>::LDS);
+    slots = xcd_slots(kern, C::LDS);
   }
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
-  grouped_gemm_dma_kernel<MODE, KB, NS, 1><<<sched_grid(p), 256, DmaCfg<KB, NS>::LDS, st>>>(p);
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8><<<sched_grid(p), 256, C::LDS, st>>>(p);
   return hipGetLastError();
 }
 
-// bf16 weights with 256-row tiles and K a multiple of 64 take the LDS-DMA
-// kernel (MOE_GEMM_DMA[_GATEUP|_DOWN]=0 selects the register-staged one, for
-// comparison); fp8 weights the register-staged one.
+// 256-row tiles with K a multiple of 64 take the LDS-DMA kernel, for bf16 or
+// fp8 weights (MOE_GEMM_DMA[_GATEUP|_DOWN]=0 selects the register-staged
+// one, for comparison); other shapes the register-staged kernel.
 template <int MODE, int BM>
 hipError_t launch_gemm_dt(const GemmParams& p, bool fp8, hipStream_t st) {
-  if (fp8) return launch_gemm<MODE, true, BM>(p, st);
   const char* v = getenv(MODE == MODE_GATEUP ? "MOE_GEMM_DMA_GATEUP" : "MOE_GEMM_DMA_DOWN");
   if (!v) v = getenv("MOE_GEMM_DMA");
   if (BM == DMA_BM && (p.K / BK) % 2 == 0 && !(v && atoi(v) == 0))
-    return launch_gemm_dma<MODE>(p, st);
-  return launch_gemm<MODE, false, BM>(p, st);
+    return fp8 ? launch_gemm_dma<MODE, true>(p, st) : launch_gemm_dma<MODE, false>(p, st);
+  return fp8 ? launch_gemm<MODE, true, BM>(p, st) : launch_gemm<MODE, false, BM>(p, st);
 }
 
 // Weight-streaming launch: one workgroup per (segment, 64 output features,

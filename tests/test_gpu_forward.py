@@ -39,6 +39,9 @@ SMALL = [
     (64, 512, 8, 2, 1408, None, False, "fp8_e4m3", None),
     (48, 256, 4, 2, 256, None, True, "bf16", None),
     (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5"),
+    # fp8 weights with 256-row tiles (the LDS-DMA kernel's fp8 path)
+    (1100, 512, 8, 2, 384, None, True, "fp8_e4m3", None),
+    (2000, 256, 4, 2, 256, 1.0, False, "fp8_e4m3", "zipf1.5"),
 ]
 
 

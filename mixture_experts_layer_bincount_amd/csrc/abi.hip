@@ -201,6 +201,19 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
   L.off_H = off;
   if (s.kind == MOE_EXPERT_SWIGLU) off = align256(off + (size_t)L.H_rows * s.d_ff * 2);
+  // partial tiles of split tail tiles of the grouped-output down projection:
+  // one per workgroup slot of the device (one workgroup per CU)
+  L.tail_cap = 0;
+  L.off_slab = off;
+  if (s.kind == MOE_EXPERT_SWIGLU) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    L.tail_cap = std::max(cus, 256);
+    off = align256(off + (size_t)L.tail_cap * 65536 * sizeof(float));
+  }
   L.grouped_combine = use_grouped_combine(s);
   L.off_Yp = off;
   if (L.grouped_combine) off = align256(off + (size_t)L.H_rows * s.d * sizeof(float));

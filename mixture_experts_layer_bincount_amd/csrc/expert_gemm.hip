@@ -92,6 +92,8 @@ struct GemmParams {
   int split_max;              // K ranges a tail tile may be cut into (1: none)
   int kunit;                  // K steps of BK per unit of the schedule
   int slots;                  // workgroups one XCD runs at once
+  float* tail_slab;           // MODE_DOWN_PERM: fp32 partial tiles of split tail tiles
+  int tail_cap;               //   (room for tail_cap tiles of 64 Ki floats)
   int group_n;                // weight tiles per expert-aligned block of the tile order
   int krot;                   // rotate each workgroup's K order (spreads L2 channels)
   int cache_aux;              // cache-policy bits of the operand loads
@@ -173,6 +175,8 @@ struct TileMap {
   int ntile;     // weight tile
   int kbeg, nk;  // K steps of this workgroup
   bool shared_e;
+  int slab;      // MODE_DOWN_PERM piece of a split tail tile: its partial-tile
+                 // slot in p.tail_slab (-1: the tile is stored directly)
 };
 
 // The workgroup's unit of the tile schedule (tile_sched.h): the segments'
@@ -181,13 +185,13 @@ struct TileMap {
 // false when the workgroup has no unit.  Must be called by all threads of
 // the workgroup.
 constexpr int kMaxSegments = 1025;  // routed experts (at most 1024) + shared
-template <int MODE, int BM>
-__device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
-  __shared__ int s_scan[4];
-  __shared__ int s_pre[kMaxSegments + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // row tiles per segment (routed experts, then the shared expert), scanned
+// Row tiles per segment (routed experts, then the shared expert), counted
+// from the device-side offsets and scanned into s_pre (s_pre[nseg] = total).
+// Must be called by all threads of the workgroup; returns the total.
+template <int BM>
+__device__ __forceinline__ int seg_prefix(const GemmParams& p, int* s_pre, int* s_scan) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nseg = p.E + (p.has_shared ? 1 : 0);
   const int per = (nseg + 255) / 256;
   const int e_lo = tid * per;
@@ -213,26 +217,45 @@ __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   }
   if (tid == 0) s_pre[nseg] = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
   __syncthreads();
-  const int Mreal = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
+  return __builtin_amdgcn_readfirstlane(s_pre[nseg]);
+}
 
-  // (uniform values: pin them to scalar registers so the buffer resources and
-  // offsets built from them need no per-lane loops)
-  SchedUnit u{};
-  const int kunits = p.K / BK / p.kunit;
-  if (!sched_unit((int64_t)Mreal * p.nt, kunits, p.slots, p.split_max,
-                  (int)(blockIdx.x % kNumXcd), (int64_t)(blockIdx.x / kNumXcd), u))
-    return false;
+// Segment, first row and weight tile of tile q (uniform values).
+template <int BM>
+__device__ __forceinline__ void tile_place(const GemmParams& p, const int* s_pre, int64_t q,
+                                           TileMap& t) {
+  const int nseg = p.E + (p.has_shared ? 1 : 0);
   int seg = 0, mslot = 0, ntile = 0;
-  sched_tile_of(u.q, s_pre, nseg, p.nt, p.group_n, seg, mslot, ntile);
+  sched_tile_of(q, s_pre, nseg, p.nt, p.group_n, seg, mslot, ntile);
   t.e = __builtin_amdgcn_readfirstlane(seg);
   t.ntile = __builtin_amdgcn_readfirstlane(ntile);
   t.m0 = __builtin_amdgcn_readfirstlane((mslot - s_pre[seg]) * BM);
-  t.kbeg = __builtin_amdgcn_readfirstlane(u.kbeg * p.kunit);
-  t.nk = __builtin_amdgcn_readfirstlane(u.nk * p.kunit);
   t.shared_e = (t.e == p.E);
   t.rows = __builtin_amdgcn_readfirstlane(t.shared_e ? (int)p.T
                                                      : p.offsets[t.e + 1] - p.offsets[t.e]);
   t.seg = __builtin_amdgcn_readfirstlane(t.shared_e ? 0 : p.offsets[t.e]);
+}
+
+// The workgroup's unit of the tile schedule (tile_sched.h) over the
+// expert-aligned tile order.  Returns false when the workgroup has no unit.
+// Must be called by all threads of the workgroup.
+template <int MODE, int BM>
+__device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
+  __shared__ int s_scan[4];
+  __shared__ int s_pre[kMaxSegments + 1];
+  const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
+  SchedUnit u{};
+  const int kunits = p.K / BK / p.kunit;
+  const int xcd = (int)(blockIdx.x % kNumXcd);
+  if (!sched_unit((int64_t)Mreal * p.nt, kunits, p.slots, p.split_max, xcd,
+                  (int64_t)(blockIdx.x / kNumXcd), u))
+    return false;
+  tile_place<BM>(p, s_pre, u.q, t);
+  t.kbeg = __builtin_amdgcn_readfirstlane(u.kbeg * p.kunit);
+  t.nk = __builtin_amdgcn_readfirstlane(u.nk * p.kunit);
+  t.slab = (MODE == MODE_DOWN_PERM && u.tail >= 0)
+               ? __builtin_amdgcn_readfirstlane(xcd * p.slots + u.tail)
+               : -1;
   return true;
 }
 
@@ -250,7 +273,7 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
 // further per i (32: contiguous rows, 64: granules interleaved with the other
 // row wave); brow: its four 32-row weight tiles; n0: first output column of
 // the tile; wn: the wave's column group.
-template <int MODE, bool FP8, int RS>
+template <int MODE, bool FP8, int RS, int BMT>
 __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
                                            const TileMap& t, int arow0, int n0, int wn,
                                            const int (&brow)[4]) {
@@ -328,6 +351,9 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
             }
             if (MODE == MODE_DOWN)
               atomicAdd(&p.y[orow * N + n], wgt * v);
+            else if (t.slab >= 0)  // piece of a split tail tile: its partial tile
+              p.tail_slab[(int64_t)t.slab * 65536 +
+                          (int64_t)(m - t.m0) * (65536 / BMT) + (n - n0)] = v;
             else
               p.y_perm[orow * N + n] = v;
           }
@@ -524,7 +550,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
   }
 #undef MOE_LOAD_STAGE
 #undef MOE_STORE_STAGE
-  store_tile<MODE, FP8, 32>(p, acc, t, arow0, n0, wn, brow);
+  store_tile<MODE, FP8, 32, BM>(p, acc, t, arow0, n0, wn, brow);
 }
 
 // ---------------------------------------------------------------------------
@@ -799,7 +825,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     else
       run(std::integral_constant<int, 0>{});
   }
-  store_tile<MODE, FP8, 64>(p, acc, t, arow0, n0, wn, brow);
+  store_tile<MODE, FP8, 64, DMA_BM>(p, acc, t, arow0, n0, wn, brow);
 }
 
 // ---------------------------------------------------------------------------
@@ -878,7 +904,7 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const int m = min(r0 + g * 16 + fr, rows - 1);
-      voA[g] = (uint32_t)((a_row<MODE>(p, TileMap{e, 0, rows, seg, 0, 0, 0, shared_e}, m) * K +
+      voA[g] = (uint32_t)((a_row<MODE>(p, TileMap{e, 0, rows, seg, 0, 0, 0, shared_e, -1}, m) * K +
                            (int64_t)kbeg * 32 + fk) * 2);
     }
     f32x4 acc0[RG], acc1[RG];
@@ -991,6 +1017,39 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
   }
 }
 
+// Tail fixup of the grouped-output down projection: the pieces of a split
+// tail tile left fp32 partial tiles in p.tail_slab; sum them in piece order
+// and store the tile's valid rows.  Workgroup b: XCD b % 8, its tail tile
+// b / 8 (the same schedule arithmetic as the GEMM, from the same offsets).
+template <int BM>
+__global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
+  constexpr int BNB = 65536 / BM;
+  __shared__ int s_scan[4];
+  __shared__ int s_pre[kMaxSegments + 1];
+  const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
+  const int xcd = (int)(blockIdx.x % kNumXcd);
+  const int r = (int)(blockIdx.x / kNumXcd);
+  int64_t qtail = 0;
+  int rem = 0, S = 1;
+  sched_tail_of_xcd((int64_t)Mreal * p.nt, xcd, p.slots, p.split_max, qtail, rem, S);
+  if (r >= rem || S <= 1) return;
+  TileMap t;
+  tile_place<BM>(p, s_pre, qtail + r, t);
+  const int n0 = t.ntile * BNB;
+  const int64_t orow0 = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
+  const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * 65536;
+  for (int idx = threadIdx.x * 4; idx < 65536; idx += 1024) {
+    const int row = idx / BNB, col = idx % BNB;
+    if (t.m0 + row >= t.rows || n0 + col >= p.N) continue;
+    float4 a = *(const float4*)(slab + idx);
+    for (int pc = 1; pc < S; ++pc) {
+      const float4 b = *(const float4*)(slab + (int64_t)pc * 65536 + idx);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *(float4*)(p.y_perm + (orow0 + row) * p.N + n0 + col) = a;
+  }
+}
+
 // Combine: y[t] = sum over kept j (in slot order) of topk_w[t, j] *
 // y_perm[slot_pos[t, j]], then + y_shared[t] (weight 1) when there is a
 // shared expert.  One thread per 4 consecutive outputs when d % 4 == 0.
@@ -1064,7 +1123,10 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = 1;
   p.slots = slots;
+  if (MODE == MODE_DOWN_PERM && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
   grouped_gemm_kernel<MODE, FP8, BM><<<sched_grid(p), 256, Tile<BM>::LDS, st>>>(p);
+  if (MODE == MODE_DOWN_PERM && p.split_max > 1)
+    tail_fixup_kernel<BM><<<(unsigned)(kNumXcd * slots), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -1085,7 +1147,10 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
+  if (MODE == MODE_DOWN_PERM && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
   grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8><<<sched_grid(p), 256, C::LDS, st>>>(p);
+  if (MODE == MODE_DOWN_PERM && p.split_max > 1)
+    tail_fixup_kernel<DMA_BM><<<(unsigned)(kNumXcd * slots), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -1154,6 +1219,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   }
   const bool fp8 = s.w_dtype == MOE_DT_FP8_E4M3;
   const int has_sh = s.has_shared ? 1 : 0;
+  float* tail_slab = H ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
+  const int tail_cap = L.tail_cap;
   // Upper bound of row tiles: sum_e ceil(rows_e / BM) <= P_max / BM + E (+ shared).
   auto mt_bound = [&](int BM) {
     return (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
@@ -1226,10 +1293,14 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   const int bn2 = 65536 / bm2;  // output columns per down tile
   g2.nt = (s.d + bn2 - 1) / bn2;
   g2.mt_max = (int)mt_bound(bm2);
-  // With the atomic combine, partial sums over K ranges add up in y, so the
-  // tiles of the last, partial round of the schedule may be split over K
-  // (pieces of at least 8 steps).
-  g2.split_max = y ? std::max(1, s.d_ff / BK / 8) : 1;
+  // The tiles of the last, partial round of the schedule may be split over K
+  // (pieces of at least 8 steps): with the atomic combine the partial sums
+  // add up in y; with the grouped output they go to the tail slab and a
+  // fixup pass sums them, which pays only for long K loops (measured: a loss
+  // at d_ff = 1408 and 2048, a gain at 14336).
+  g2.split_max = (y || s.d_ff >= 4096) ? std::max(1, s.d_ff / BK / 8) : 1;
+  g2.tail_slab = tail_slab;
+  g2.tail_cap = tail_cap;
   if (stream_down) {
     // K pieces so that about 8192 waves stream W2 (each at least 16 steps)
     const int64_t waves = (int64_t)nseg * ((s.d + 63) / 64) * 4;

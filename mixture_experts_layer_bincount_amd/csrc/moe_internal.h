@@ -40,6 +40,8 @@ struct WsLayout {
   size_t off_perm_w;     // fp32  [P_max]
   size_t off_slot_pos;   // int32 [T*k]
   size_t off_H;          // bf16  [H_rows, d_ff]
+  int tail_cap;          // partial tiles the tail slab holds
+  size_t off_slab;       // fp32  [tail_cap, 65536] split tail tiles (SwiGLU)
   bool grouped_combine;  // moe_forward: grouped output + combine instead of atomics
   size_t off_Yp;         // fp32  [H_rows, d] (grouped_combine only)
   size_t total;

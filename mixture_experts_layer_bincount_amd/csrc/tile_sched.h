@@ -36,6 +36,9 @@ struct SchedUnit {
   int64_t q;  // tile, 0 .. R-1
   int kbeg;   // first K unit
   int nk;     // K units
+  int S;      // K pieces of the tile (1: a whole tile)
+  int tail;   // for a piece of a split tile: its index among the XCD's tail
+              // units, rem * S <= slots of them (-1 for a whole tile)
 };
 
 // Tile q -> (segment, row tile, weight tile) in the expert-aligned order
@@ -80,6 +83,18 @@ constexpr int64_t sched_units_of_xcd(int64_t R, int xcd, int slots, int split_ma
   return full + (int64_t)rem * sched_tail_split(rem, slots, split_max);
 }
 
+// The XCD's tail: its tiles after the whole rounds (rem), and the K pieces
+// each is cut into (S); tail unit j = r * S + piece covers tile q0 + full + r.
+constexpr void sched_tail_of_xcd(int64_t R, int xcd, int slots, int split_max, int64_t& qtail,
+                                 int& rem, int& S) {
+  const int64_t q0 = R * xcd / kNumXcd, q1 = R * (xcd + 1) / kNumXcd;
+  const int64_t n = q1 - q0;
+  const int64_t full = n / slots * slots;
+  qtail = q0 + full;
+  rem = (int)(n - full);
+  S = sched_tail_split(rem, slots, split_max);
+}
+
 // Upper bound of the units of any XCD given an upper bound of R (grid size).
 constexpr int64_t sched_units_bound(int64_t R_max, int slots) {
   return (R_max + kNumXcd - 1) / kNumXcd + slots;
@@ -93,6 +108,7 @@ constexpr bool sched_unit(int64_t R, int kunits, int slots, int split_max, int x
   const int64_t n = q1 - q0;
   const int64_t full = n / slots * slots;
   int piece = 0, S = 1;
+  u.tail = -1;
   if (i < full) {
     u.q = q0 + i;
   } else {
@@ -102,7 +118,9 @@ constexpr bool sched_unit(int64_t R, int kunits, int slots, int split_max, int x
     if (j >= (int64_t)rem * S) return false;
     u.q = q0 + full + j / S;
     piece = (int)(j % S);
+    if (S > 1) u.tail = (int)j;
   }
+  u.S = S;
   u.kbeg = (int)((int64_t)kunits * piece / S);
   u.nk = (int)((int64_t)kunits * (piece + 1) / S) - u.kbeg;
   return true;

@@ -43,6 +43,17 @@ static int check(const std::vector<int>& tiles_per_seg, int nt, int gn, int kuni
                Mreal, nt, gn, x, (long long)i, (long long)u.q, seg, m, n, u.kbeg, u.nk);
         return 1;
       }
+      {  // tail bookkeeping: the unit's tail index names its tile and piece
+        int64_t qtail = 0;
+        int rem = 0, S = 0;
+        sched_tail_of_xcd(R, x, slots, split_max, qtail, rem, S);
+        if (u.S != (u.tail >= 0 ? S : u.S) || (u.tail >= 0) != (u.q >= qtail && S > 1) ||
+            (u.tail >= 0 && (u.tail >= rem * S || qtail + u.tail / S != u.q ||
+                             u.tail >= slots))) {
+          printf("FAIL tail bookkeeping M=%d nt=%d x=%d i=%lld\n", Mreal, nt, x, (long long)i);
+          return 1;
+        }
+      }
       if (u.nk < kunits / split_max) {
         printf("FAIL piece shorter than split_max allows M=%d nt=%d\n", Mreal, nt);
         return 1;

@@ -42,6 +42,10 @@ SMALL = [
     # fp8 weights with 256-row tiles (the LDS-DMA kernel's fp8 path)
     (1100, 512, 8, 2, 384, None, True, "fp8_e4m3", None),
     (2000, 256, 4, 2, 256, 1.0, False, "fp8_e4m3", "zipf1.5"),
+    # long down-projection K with few tiles per XCD: every tile is a split
+    # tail tile summed by the fixup pass (grouped output), bf16 and fp8
+    (600, 512, 4, 2, 4096, None, True, "bf16", None),
+    (600, 512, 4, 2, 4096, None, False, "fp8_e4m3", None),
 ]
 
 

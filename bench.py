@@ -68,23 +68,25 @@ def _traffic_from_profile(kernel_src: str, launches_bytes_key: str):
     return rec.get(launches_bytes_key)
 
 
-def cpu_baseline(wl, host_experts, n_tokens: int) -> dict:
+def cpu_baseline(wl, host_experts, n_tokens: int, repeats: int) -> dict:
     """The oracle as it stands, on the first n_tokens tokens of the workload
-    (routing, dispatch, masked per-expert loop, combine; float64)."""
+    (routing, dispatch, masked per-expert loop, combine; float64), run
+    `repeats` times."""
     import oracle
     c = wl.cfg
     n_tokens = min(n_tokens, c.T)
     x = wl.x()[:n_tokens]
     W_g = wl.W_g()
     t0 = time.perf_counter()
-    oracle.forward(x, W_g, wl.b_g(), c.k, c.E, lambda e: host_experts[e], kind=c.kind,
-                   C=oracle.capacity(n_tokens, c.E, c.k, c.cf))
+    for _ in range(repeats):
+        oracle.forward(x, W_g, wl.b_g(), c.k, c.E, lambda e: host_experts[e], kind=c.kind,
+                       C=oracle.capacity(n_tokens, c.E, c.k, c.cf))
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": _blas_threads(),
+    return {"value": n_tokens * repeats / dt, "unit": "tokens/s", "cores": _blas_threads(),
             "kind": "oracle",
             "sample": f"first {n_tokens} of the {c.T} tokens of the {c.name} workload, whole "
                       f"layer (router, top-k, bincount, dispatch, masked per-expert loop, "
-                      f"combine) in float64 NumPy; {dt:.1f} s on {_cpu_model()}"}
+                      f"combine) in float64 NumPy, {repeats} runs; {dt:.1f} s on {_cpu_model()}"}
 
 
 def main() -> int:
@@ -95,6 +97,7 @@ def main() -> int:
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -204,6 +207,21 @@ def main() -> int:
                                       "tflops": flops_down / (dn_ms * 1e-3) / 1e12}},
     }
 
+    # ---- load statistics of this step's routing (tutorial §4.2 / §4.3: the
+    # imbalance max/(min + 1e-6) and the LPT packing of the expert loads onto
+    # 8 devices, by the library's host functions), on the raw counts and on
+    # the kept (capacity-limited) rows
+    kept_rows = np.diff(layer.offsets.cpu().numpy()).tolist()
+    stats = {}
+    for name, load in (("counts", counts), ("kept", kept_rows)):
+        _, bins = moe.moe_lpt_pack(load, 8)
+        stats[name] = {"imbalance": moe.moe_load_imbalance(load),
+                       "max_over_mean": max(load) / (sum(load) / len(load)),
+                       "empty_experts": int(sum(1 for v in load if v == 0)),
+                       "lpt_8_bins": bins,
+                       "lpt_8_max_over_mean": max(bins) / (sum(bins) / len(bins))}
+    result["load_stats"] = stats
+
     # ---- decode-shaped layer: the same weights, the first 64 tokens
     if not args.no_decode and cfg.name == "mixtral":
         dcfg = get_config("decode")
@@ -233,7 +251,7 @@ def main() -> int:
     # ---- CPU oracle baseline on a bounded sample
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, host_experts, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(wl, host_experts, args.cpu_tokens, args.cpu_repeats)
     else:
         result["cpu_baseline"] = None
 

@@ -15,22 +15,26 @@
 // A shared expert (iopenshare §1.4: always-active experts) is expert index E
 // with T rows, row t = token t, weight 1, hidden rows P_max .. P_max + T.
 //
-// Workgroup tile: 128 activation rows x 512 weight rows, K in steps of 32;
-// 256 threads = 4 waves, each wave all 128 rows x its own 128 weight rows =
-// 4 x 4 MFMA tiles of 32x32 (256 accumulators per lane).  In MODE_GATEUP a
-// wave's 128 weight rows are 64 rows of W1 and the same 64 rows of W3, so the
-// SwiGLU happens in registers; the product is computed transposed
-// (weights as the MFMA A operand) so each lane holds 4 consecutive hidden
-// columns of one row and stores them as one 8-byte write.
-// Pipeline: double-buffered LDS (padded rows, conflict-free 16-byte fragment
-// reads) fed from three register stages, so each global load has two K steps
-// of MFMAs to land; fragments of the next 16 K are read from LDS under the
-// current MFMAs; one barrier per K step.
+// Workgroup tile: 256 activation rows x 256 weight rows, K in steps of 64;
+// 256 threads = 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32x32, 256 fp32
+// accumulators per lane).  A wave's activation rows are the 32-row granules
+// wm, wm + 2, wm + 4, wm + 6 of the tile, and it runs only the granules that
+// hold rows of the segment (partial tiles cost in proportion to their rows).
+// In MODE_GATEUP a wave's 128 weight rows are 64 rows of W1 and the same 64
+// rows of W3, so the SwiGLU happens in registers; the product is computed
+// transposed (weights as the MFMA A operand) so each lane holds 4
+// consecutive hidden columns of one row and stores them as one 8-byte write.
+// Operands move global -> LDS by buffer_load ... lds (two 64-deep stages,
+// XOR-swizzled rows, no bank conflicts on the 16-byte fragment reads); the
+// next 32-deep slice's fragments are read under the current slice's MFMAs;
+// one barrier per step.  fp8 (e4m3) weights land in LDS as bytes and are
+// widened exactly to bf16 in registers; their scales apply in the epilogue.
 // Tile order (tile_sched.h): the real tiles, counted on the device, are dealt
-// evenly to the XCDs in 8 (row tiles) x 4 (weight tiles) blocks, so the
-// workgroups one XCD runs at the same time share both operands in its L2;
-// with the atomic combine the tiles of the last, partial round are split over
-// K and their partial sums added by the same atomics.
+// evenly to the XCDs in expert-aligned blocks, so the workgroups one XCD runs
+// at the same time share operands in its L2.  The tiles of the last, partial
+// round may be split over K: their partial sums are added by the atomic
+// combine, or (grouped output) summed from a partial-tile slab by a fixup
+// pass.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,22 +51,9 @@ enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_DOWN_PERM = 2 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Tile shapes: BM activation rows x BNB weight rows with BM * BNB = 65536
-// (four waves of 128 x 128): 128 x 512 (waves split the weight rows) or
-// 256 x 256 (2 x 2 waves).
-constexpr int BK = 32;        // K per step
-constexpr int LDSK = BK + 8;  // padded LDS row, bf16 elements (80 bytes)
-template <int BM>
-struct Tile {
-  static constexpr int BNB = 65536 / BM;     // weight rows per tile
-  static constexpr int WM = BM / 128;        // waves along the activation rows
-  static constexpr int WN = 4 / WM;          // waves along the weight rows
-  static constexpr int NA = BM / 64;         // 16-byte A loads per thread and K step
-  static constexpr int NB = BNB / 64;        // 16-byte B loads per thread and K step
-  static constexpr int A_STAGE = BM * LDSK;
-  static constexpr int B_STAGE = BNB * LDSK;
-  static constexpr size_t LDS = (size_t)2 * (A_STAGE + B_STAGE) * sizeof(uint16_t);
-};
+// Tiles: 256 activation rows x 256 weight rows (four waves of 128 x 128);
+// K is counted in units of BK (the schedule's K pieces are whole multiples).
+constexpr int BK = 32;
 
 struct GemmParams {
   const uint16_t* A;          // GATEUP: x [T, K]; DOWN*: H [H_rows, K]
@@ -402,158 +393,6 @@ __device__ __forceinline__ void mfma_slice(f32x16 (&acc)[4][4], const bf16x8 (&a
 }
 
 // ---------------------------------------------------------------------------
-// Register-staged kernel (used for fp8 weights, which are widened to bf16 on
-// their way into LDS, and as the fallback of the LDS-DMA kernel).
-template <int MODE, bool FP8, int BM>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmParams p) {
-  using TL = Tile<BM>;
-  constexpr int BNB = TL::BNB, NA = TL::NA, NB = TL::NB;
-  constexpr int A_STAGE = TL::A_STAGE, B_STAGE = TL::B_STAGE;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* As = lds;                    // [2][BM][LDSK]
-  uint16_t* Bs = lds + 2 * A_STAGE;      // [2][BNB][LDSK]
-
-  TileMap t;
-  if (!map_tile<MODE, BM>(p, t)) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int K = p.K, N = p.N, kbeg = t.kbeg, nk = t.nk;
-
-  // ---- operand sources as buffer loads: one scalar resource per operand
-  // (and per expert matrix), a 32-bit byte offset per thread and row that
-  // stays fixed over K, and the K step in the scalar offset.
-  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
-  const int lr = tid >> 2;         // 0..63: rows lr + 64 i
-  const int kc = (tid & 3) * 8;    // element offset within BK
-  const __amdgpu_buffer_rsrc_t rsA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, (int)p.A_bytes, kBufferWord3);
-  uint32_t voA[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int m = min(t.m0 + lr + 64 * i, t.rows - 1);
-    voA[i] = (uint32_t)((a_row<MODE>(p, t, m) * K + kc) * 2);
-  }
-  // B row r of the tile.  GATEUP: rows < BNB/2 are W1 rows n0 + r, the rest
-  // W3 rows n0 + r - BNB/2 (n0 = ntile * BNB/2).  DOWN: W2 rows n0 + r
-  // (n0 = ntile * BNB).  Rows past N are clamped (outputs masked).
-  const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
-  const int64_t ebytes = (int64_t)N * K * WB;  // one expert matrix (< 2^31)
-  const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
-  const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)(t.shared_e ? p.B0s : p.B0) + eoff), (short)0, (int)ebytes, kBufferWord3);
-  __amdgpu_buffer_rsrc_t rsB1 = rsB0;
-  if (MODE == MODE_GATEUP)
-    rsB1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)(t.shared_e ? p.B1s : p.B1) + eoff), (short)0, (int)ebytes, kBufferWord3);
-  uint32_t voB[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int r = lr + 64 * i;
-    int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
-    n = min(n, N - 1);
-    voB[i] = (uint32_t)((n * K + kc) * WB);
-  }
-  // In GATEUP, B loads i < NB/2 come from W1 and the rest from W3.
-
-  // Three register stages of global loads, so a load has two K steps of MFMAs
-  // to land.  (static_for, not a pragma-unrolled loop: this compiler
-  // otherwise keeps the stage arrays in scratch memory.)
-  uint4 ra_0[NA], rb_0[NB], ra_1[NA], rb_1[NB], ra_2[NA], rb_2[NB];
-#define MOE_LOAD_STAGE(S, KT)                                                           \
-  do {                                                                                  \
-    const int kstep_ = __builtin_amdgcn_readfirstlane(kbeg + (KT));                     \
-    static_for<NA>([&](auto i_) { ra_##S[i_] = buf_load16(rsA, voA[i_], kstep_ * BK * 2); }); \
-    static_for<NB>([&](auto i_) {                                                       \
-      rb_##S[i_] = load_b8<FP8>((MODE == MODE_GATEUP && i_ >= NB / 2) ? rsB1 : rsB0,    \
-                                voB[i_], kstep_ * BK * WB);                             \
-    });                                                                                 \
-  } while (0)
-#define MOE_STORE_STAGE(S, BUF)                                                         \
-  do {                                                                                  \
-    uint16_t* a_ = As + (BUF) * A_STAGE;                                                \
-    uint16_t* b_ = Bs + (BUF) * B_STAGE;                                                \
-    static_for<NA>([&](auto i_) { *(uint4*)&a_[(lr + 64 * i_) * LDSK + kc] = ra_##S[i_]; }); \
-    static_for<NB>([&](auto i_) { *(uint4*)&b_[(lr + 64 * i_) * LDSK + kc] = rb_##S[i_]; }); \
-  } while (0)
-
-  // ---- the wave's 128 activation rows and 128 weight rows (4 tiles of 32).
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const int arow0 = wm * 128;
-  int brow[4];
-  wave_brows<MODE, BNB>(wn, brow);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  auto compute = [&](int buf) {
-    const uint16_t* a = As + buf * A_STAGE;
-    const uint16_t* b = Bs + buf * B_STAGE;
-    bf16x8 af[2][4], bfr[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)&a[(arow0 + i * 32 + frow) * LDSK + fk];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + fk];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) {  // fragments of the next 16 K, read under this step's MFMAs
-        const int ko = (kk + 1) * 16 + fk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[cur ^ 1][i] = *(const bf16x8*)&a[(arow0 + i * 32 + frow) * LDSK + ko];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[cur ^ 1][j] = *(const bf16x8*)&b[(brow[j] + frow) * LDSK + ko];
-      }
-      mfma_slice<MODE>(acc, af[cur], bfr[cur]);
-    }
-  };
-
-  // ---- main loop, unrolled by the three register stages.  At the top of an
-  // iteration LDS buffer kt & 1 holds step kt, stage 1 holds step kt + 1 and
-  // stage 2 step kt + 2 (possibly still in flight); stage 0 is free.  Each
-  // sub-step computes one K step, moves the next stage into the other LDS
-  // buffer and reloads the stage it freed three steps ahead.  The loop has a
-  // single exit (no early breaks: those make the accumulators merge at several
-  // points, which this compiler answers with register copies); the 0..2
-  // leftover steps follow in straight-line code.  One barrier per step.
-  if (nk > 0) {
-    MOE_LOAD_STAGE(0, 0);
-    if (nk > 1) MOE_LOAD_STAGE(1, 1);
-    if (nk > 2) MOE_LOAD_STAGE(2, 2);
-    MOE_STORE_STAGE(0, 0);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 3 <= nk; kt += 3) {
-      compute(kt & 1);
-      MOE_STORE_STAGE(1, (kt + 1) & 1);
-      __syncthreads();
-      if (kt + 3 < nk) MOE_LOAD_STAGE(0, kt + 3);
-      compute((kt + 1) & 1);
-      MOE_STORE_STAGE(2, kt & 1);
-      __syncthreads();
-      if (kt + 4 < nk) MOE_LOAD_STAGE(1, kt + 4);
-      compute(kt & 1);
-      if (kt + 3 < nk) MOE_STORE_STAGE(0, (kt + 1) & 1);
-      __syncthreads();
-      if (kt + 5 < nk) MOE_LOAD_STAGE(2, kt + 5);
-    }
-    const int rem = nk - kt;
-    if (rem >= 1) {
-      compute(kt & 1);
-      if (rem >= 2) {
-        MOE_STORE_STAGE(1, (kt + 1) & 1);
-        __syncthreads();
-        compute((kt + 1) & 1);
-      }
-    }
-  }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
-  store_tile<MODE, FP8, 32, BM>(p, acc, t, arow0, n0, wn, brow);
-}
-
-// ---------------------------------------------------------------------------
 // LDS-DMA kernel for bf16 weights: 256 x 256 tiles (2 x 2 waves of 128 x 128),
 // operands moved global -> LDS by buffer_load ... lds (no register staging,
 // no LDS write instructions), NS stage buffers of KB-deep K steps, filled
@@ -828,163 +667,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   store_tile<MODE, FP8, 64, DMA_BM>(p, acc, t, arow0, n0, wn, brow);
 }
 
-// ---------------------------------------------------------------------------
-// Weight-streaming kernel for few rows per expert (decode-sized batches).
-// With ~16 rows per expert the GEMMs are bound by reading the weights once
-// from HBM; tiles of 128 or 256 rows would spend most MFMAs on padding and
-// keep too few bytes in flight.  Here every wave owns 16 weight rows
-// (16 output features) of one expert and walks K in steps of 32, loading its
-// weight fragments straight from global memory into MFMA operand registers
-// (16x16x32 bf16: lane l holds 8 consecutive K of weight row l % 16), D steps
-// ahead, with no LDS and no barriers.  The expert's activation rows (at most
-// 16 * RG per pass; more rows take further passes) come through the same
-// kind of fragment loads and stay cache-resident, as every wave of the
-// expert reads the same rows.  The product is computed transposed (weights
-// as the A operand), so lane l ends with activation row l % 16 and 4
-// consecutive output features 4 (l / 16) .. + 3.
-//   GATEUP  W1 and W3 rows of the same 16 hidden features; SwiGLU in registers
-//   DOWN    W2 rows of 16 output features; K may be split over workgroups
-//           (p.split_max pieces), whose partial sums the atomic combine adds
-//   DOWN_PERM  as DOWN into the grouped output (K not split)
-// Workgroup b: segment (expert, or E for the shared expert), a block of 64
-// output features (4 waves x 16) and a K piece.
-template <bool FP8>
-__device__ __forceinline__ bf16x8 load_w8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  const uint4 v = load_b8<FP8>(r, voff, soff);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-template <int MODE, bool FP8, int RG, int D>
-__global__ __launch_bounds__(256) void grouped_stream_kernel(GemmParams p) {
-  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int K = p.K, N = p.N;
-  const int ncb = (N + 63) / 64;
-  const int ks = (MODE == MODE_DOWN) ? p.split_max : 1;
-  int b = (int)blockIdx.x;
-  const int kp = b % ks;
-  b /= ks;
-  const int cb = b % ncb;
-  const int e = b / ncb;  // segment
-  const bool shared_e = (e == p.E);
-  const int rows = shared_e ? (int)p.T : p.offsets[e + 1] - p.offsets[e];
-  const int seg = shared_e ? 0 : p.offsets[e];
-  const int n0 = cb * 64 + wave * 16;
-  if (rows <= 0 || n0 >= N) return;
-  const int ksteps = K / 32;
-  const int kbeg = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps * kp / ks));
-  const int nk = __builtin_amdgcn_readfirstlane((int)((int64_t)ksteps * (kp + 1) / ks) - kbeg);
-
-  const int64_t ebytes = (int64_t)N * K * WB;
-  const int64_t eoff = shared_e ? 0 : (int64_t)e * ebytes;
-  const __amdgpu_buffer_rsrc_t rsW0 =
-      uniform_rsrc((const char*)(shared_e ? p.B0s : p.B0) + eoff, ebytes);
-  __amdgpu_buffer_rsrc_t rsW1 = rsW0;
-  if (MODE == MODE_GATEUP)
-    rsW1 = uniform_rsrc((const char*)(shared_e ? p.B1s : p.B1) + eoff, ebytes);
-  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A, p.A_bytes);
-  const int fr = lane & 15;         // fragment row: weight row / activation row
-  const int fk = (lane >> 4) * 8;   // first K element of the lane within a step
-  const uint32_t voW = (uint32_t)(((int64_t)(n0 + fr) * K + (int64_t)kbeg * 32 + fk) * WB);
-
-  float sc0 = 1.f, sc1 = 1.f;
-  if (FP8) {
-    const int gi = n0 / kFp8Group;  // the wave's 16 rows share one scale
-    sc0 = shared_e ? p.sc0s[gi] : p.sc0[(int64_t)e * (N / kFp8Group) + gi];
-    if (MODE == MODE_GATEUP) sc1 = shared_e ? p.sc1s[gi] : p.sc1[(int64_t)e * (N / kFp8Group) + gi];
-  }
-
-  const int krot = p.krot ? __builtin_amdgcn_readfirstlane(
-                                (int)((((unsigned)blockIdx.x * 4u + wave) * 2654435761u >> 8) %
-                                      (unsigned)nk))
-                          : 0;
-  for (int r0 = 0; r0 < rows; r0 += 16 * RG) {
-    uint32_t voA[RG];
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      const int m = min(r0 + g * 16 + fr, rows - 1);
-      voA[g] = (uint32_t)((a_row<MODE>(p, TileMap{e, 0, rows, seg, 0, 0, 0, shared_e, -1}, m) * K +
-                           (int64_t)kbeg * 32 + fk) * 2);
-    }
-    f32x4 acc0[RG], acc1[RG];
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    bf16x8 w0[D], w1[D], xa[D][RG];
-    // step s of this piece (clamped to the last step: the extra loads past
-    // the end reread data already in the caches and are never used), walked
-    // from a per-wave rotated start so that concurrent waves, whose weight
-    // rows lie a power-of-two stride apart, spread over the memory channels
-    auto load = [&](auto slot, int s) __attribute__((always_inline)) {
-      int st = min(s, nk - 1) + krot;
-      st = __builtin_amdgcn_readfirstlane(st >= nk ? st - nk : st);
-      w0[slot] = load_w8<FP8>(rsW0, voW, st * 32 * WB);
-      if (MODE == MODE_GATEUP) w1[slot] = load_w8<FP8>(rsW1, voW, st * 32 * WB);
-#pragma unroll
-      for (int g = 0; g < RG; ++g)
-        xa[slot][g] = __builtin_bit_cast(bf16x8, buf_load16(rsA, voA[g], st * 64));
-    };
-    auto mma = [&](auto slot) __attribute__((always_inline)) {
-#pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0[slot], xa[slot][g], acc0[g], 0, 0, 0);
-        if (MODE == MODE_GATEUP)
-          acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1[slot], xa[slot][g], acc1[g], 0, 0, 0);
-      }
-    };
-    static_for<D>([&](auto s) { load(s, s); });
-    int kt = 0;
-    for (; kt + D <= nk; kt += D) {  // single exit; slots stay compile-time
-      static_for<D>([&](auto s) {
-        mma(s);
-        load(s, kt + s + D);
-      });
-    }
-    static_for<D>([&](auto s) {
-      if (kt + s < nk) mma(s);
-    });
-
-    // epilogue: lane holds activation row r0 + 16 g + fr, features n0 + fk/2 .. + 3
-    const int nf = n0 + (lane >> 4) * 4;
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      const int m = r0 + g * 16 + fr;
-      if (m >= rows) continue;
-      if (MODE == MODE_GATEUP) {
-        const int64_t hrow = (shared_e ? p.P_max : (int64_t)seg) + m;
-        uint32_t hb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = acc0[g][r] * sc0;
-          const float u = acc1[g][r] * sc1;
-          hb[r] = f32_to_bf16_bits(a / (1.f + __expf(-a)) * u);
-        }
-        uint2 v;
-        v.x = hb[0] | (hb[1] << 16);
-        v.y = hb[2] | (hb[3] << 16);
-        *(uint2*)(p.H + hrow * N + nf) = v;
-      } else if (MODE == MODE_DOWN) {
-        int64_t orow = m;
-        float wgt = 1.f;
-        if (!shared_e) {
-          orow = p.perm_token[seg + m];
-          wgt = p.perm_w[seg + m] * sc0;
-        } else {
-          wgt = sc0;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) atomicAdd(&p.y[orow * N + nf + r], wgt * acc0[g][r]);
-      } else {
-        float4 v = make_float4(acc0[g][0] * sc0, acc0[g][1] * sc0, acc0[g][2] * sc0, acc0[g][3] * sc0);
-        *(float4*)(p.y_perm + ((shared_e ? p.P_max : (int64_t)seg) + m) * N + nf) = v;
-      }
-    }
-  }
-}
-
 // Linear+bias experts in fp32 (the tutorial's nn.Linear(d, d) experts, §4.1).
 // One thread per (grouped row, output feature); MODE_DOWN adds w * out into y.
 template <int MODE>
@@ -1019,16 +701,20 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
 
 // Tail fixup of the grouped-output down projection: the pieces of a split
 // tail tile left fp32 partial tiles in p.tail_slab; sum them in piece order
-// and store the tile's valid rows.  Workgroup b: XCD b % 8, its tail tile
+// and store the tile's valid rows.  kFixBands workgroups share a tile, one
+// band of rows each: workgroup b is XCD b % 8, then (tail tile, band) of
 // b / 8 (the same schedule arithmetic as the GEMM, from the same offsets).
+constexpr int kFixBands = 16;
 template <int BM>
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   constexpr int BNB = 65536 / BM;
+  constexpr int BAND = 65536 / kFixBands;  // floats per band
   __shared__ int s_scan[4];
   __shared__ int s_pre[kMaxSegments + 1];
-  const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
   const int xcd = (int)(blockIdx.x % kNumXcd);
-  const int r = (int)(blockIdx.x / kNumXcd);
+  const int r = (int)(blockIdx.x / kNumXcd / kFixBands);
+  const int band = (int)(blockIdx.x / kNumXcd % kFixBands);
+  const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
   int64_t qtail = 0;
   int rem = 0, S = 1;
   sched_tail_of_xcd((int64_t)Mreal * p.nt, xcd, p.slots, p.split_max, qtail, rem, S);
@@ -1038,15 +724,26 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   const int n0 = t.ntile * BNB;
   const int64_t orow0 = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
   const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * 65536;
-  for (int idx = threadIdx.x * 4; idx < 65536; idx += 1024) {
-    const int row = idx / BNB, col = idx % BNB;
-    if (t.m0 + row >= t.rows || n0 + col >= p.N) continue;
-    float4 a = *(const float4*)(slab + idx);
-    for (int pc = 1; pc < S; ++pc) {
-      const float4 b = *(const float4*)(slab + (int64_t)pc * 65536 + idx);
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  constexpr int PER = BAND / 4 / 256;  // float4 per thread
+  float4 a[PER];
+  int idx[PER];
+#pragma unroll
+  for (int v = 0; v < PER; ++v) {
+    idx[v] = band * BAND + (v * 256 + (int)threadIdx.x) * 4;
+    a[v] = *(const float4*)(slab + idx[v]);
+  }
+  for (int pc = 1; pc < S; ++pc) {
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      const float4 b = *(const float4*)(slab + (int64_t)pc * 65536 + idx[v]);
+      a[v].x += b.x; a[v].y += b.y; a[v].z += b.z; a[v].w += b.w;
     }
-    *(float4*)(p.y_perm + (orow0 + row) * p.N + n0 + col) = a;
+  }
+#pragma unroll
+  for (int v = 0; v < PER; ++v) {
+    const int row = idx[v] / BNB, col = idx[v] % BNB;
+    if (t.m0 + row < t.rows && n0 + col < p.N)
+      *(float4*)(p.y_perm + (orow0 + row) * p.N + n0 + col) = a[v];
   }
 }
 
@@ -1109,26 +806,6 @@ inline unsigned sched_grid(const GemmParams& p) {
   return (unsigned)(kNumXcd * sched_units_bound((int64_t)p.mt_max * p.nt, p.slots));
 }
 
-template <int MODE, bool FP8, int BM>
-hipError_t launch_gemm(const GemmParams& p0, hipStream_t st) {
-  if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  const void* kern = (const void*)grouped_gemm_kernel<MODE, FP8, BM>;
-  static int slots = 0;  // opt in to more than 64 KiB of LDS, once per process
-  if (!slots) {
-    hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)Tile<BM>::LDS);
-    if (err != hipSuccess) return err;
-    slots = xcd_slots(kern, Tile<BM>::LDS);
-  }
-  GemmParams p = p0;
-  p.kunit = 1;
-  p.slots = slots;
-  if (MODE == MODE_DOWN_PERM && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
-  grouped_gemm_kernel<MODE, FP8, BM><<<sched_grid(p), 256, Tile<BM>::LDS, st>>>(p);
-  if (MODE == MODE_DOWN_PERM && p.split_max > 1)
-    tail_fixup_kernel<BM><<<(unsigned)(kNumXcd * slots), 256, 0, st>>>(p);
-  return hipGetLastError();
-}
 
 // The LDS-DMA kernel: 64-deep K steps in two stages.
 template <int MODE, bool FP8>
@@ -1150,50 +827,10 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (MODE == MODE_DOWN_PERM && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
   grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8><<<sched_grid(p), 256, C::LDS, st>>>(p);
   if (MODE == MODE_DOWN_PERM && p.split_max > 1)
-    tail_fixup_kernel<DMA_BM><<<(unsigned)(kNumXcd * slots), 256, 0, st>>>(p);
+    tail_fixup_kernel<DMA_BM><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
-// 256-row tiles with K a multiple of 64 take the LDS-DMA kernel, for bf16 or
-// fp8 weights (MOE_GEMM_DMA[_GATEUP|_DOWN]=0 selects the register-staged
-// one, for comparison); other shapes the register-staged kernel.
-template <int MODE, int BM>
-hipError_t launch_gemm_dt(const GemmParams& p, bool fp8, hipStream_t st) {
-  const char* v = getenv(MODE == MODE_GATEUP ? "MOE_GEMM_DMA_GATEUP" : "MOE_GEMM_DMA_DOWN");
-  if (!v) v = getenv("MOE_GEMM_DMA");
-  if (BM == DMA_BM && (p.K / BK) % 2 == 0 && !(v && atoi(v) == 0))
-    return fp8 ? launch_gemm_dma<MODE, true>(p, st) : launch_gemm_dma<MODE, false>(p, st);
-  return fp8 ? launch_gemm<MODE, true, BM>(p, st) : launch_gemm<MODE, false, BM>(p, st);
-}
-
-// Weight-streaming launch: one workgroup per (segment, 64 output features,
-// K piece); p.split_max = K pieces (MODE_DOWN only).
-template <int MODE, bool FP8>
-hipError_t launch_stream(const GemmParams& p, int nseg, hipStream_t st) {
-  const int64_t grid = (int64_t)nseg * ((p.N + 63) / 64) * (MODE == MODE_DOWN ? p.split_max : 1);
-  if (grid <= 0) return hipSuccess;
-  const char* dv = getenv("MOE_STREAM_D");  // prefetch depth (tuning)
-  const int D = dv ? atoi(dv) : 8;
-  if (D == 4)
-    grouped_stream_kernel<MODE, FP8, 2, 4><<<(unsigned)grid, 256, 0, st>>>(p);
-  else if (D == 12)
-    grouped_stream_kernel<MODE, FP8, 2, 12><<<(unsigned)grid, 256, 0, st>>>(p);
-  else
-    grouped_stream_kernel<MODE, FP8, 2, 8><<<(unsigned)grid, 256, 0, st>>>(p);
-  return hipGetLastError();
-}
-
-// Row-tile height of the grouped GEMMs: 256 (256 x 256 tiles; LDS-DMA kernel
-// for bf16 weights) by default, or 128 (128 x 512 tiles, register-staged);
-// MOE_GEMM_BM, MOE_GEMM_BM_GATEUP and MOE_GEMM_BM_DOWN override it (tuning).
-int gemm_bm(int mode, int64_t rows_per_expert) {
-  const char* v = getenv(mode == MODE_GATEUP ? "MOE_GEMM_BM_GATEUP" : "MOE_GEMM_BM_DOWN");
-  if (!v) v = getenv("MOE_GEMM_BM");
-  if (v) return atoi(v) == 128 ? 128 : 256;
-  // few rows per expert (decode): 128-row tiles waste half as many MFMAs on
-  // padding rows, and the weights, not the MFMAs, set the time
-  return rows_per_expert < 128 ? 128 : 256;
-}
 
 }  // namespace
 
@@ -1222,11 +859,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   float* tail_slab = H ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
   const int tail_cap = L.tail_cap;
   // Upper bound of row tiles: sum_e ceil(rows_e / BM) <= P_max / BM + E (+ shared).
-  auto mt_bound = [&](int BM) {
-    return (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
-  };
-  const int64_t rows_per_expert = L.P_max / std::max(1, s.E);
-  const int bm1 = gemm_bm(MODE_GATEUP, rows_per_expert), bm2 = gemm_bm(MODE_DOWN, rows_per_expert);
+  constexpr int BM = DMA_BM;
+  const int64_t mt_bound = (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
 
   GemmParams g{};
   g.perm_token = perm_token;
@@ -1236,7 +870,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.P_max = L.P_max;
   g.E = s.E;
   g.has_shared = has_sh;
-  g.mt_max = (int)mt_bound(bm1);
+  g.mt_max = (int)mt_bound;
   g.split_max = 1;
   {
     const char* kr = getenv("MOE_GEMM_KROT");
@@ -1255,24 +889,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.H = (uint16_t*)H;
   g.K = s.d;
   g.N = s.d_ff;
-  const int bn1 = 65536 / bm1 / 2;  // hidden columns per gate/up tile
+  const int bn1 = 128;  // hidden columns per gate/up tile (128 of W1 + 128 of W3)
   g.nt = (s.d_ff + bn1 - 1) / bn1;
-  // Few rows per expert (decode): the weight-streaming kernel for the gate/up
-  // projection (MOE_STREAM=0 turns it off).  The tiled down projection with
-  // its K-split tail measures faster than the streaming one at decode size
-  // (MOE_STREAM_DOWN=1 selects the latter, for comparison).
-  const char* sv = getenv("MOE_STREAM");
-  const char* sdv = getenv("MOE_STREAM_DOWN");
-  const bool stream = rows_per_expert <= 32 && !(sv && atoi(sv) == 0);
-  const bool stream_down = stream && sdv && atoi(sdv) == 1;
-  const int nseg = s.E + has_sh;
-  hipError_t err;
-  if (stream)
-    err = fp8 ? launch_stream<MODE_GATEUP, true>(g, nseg, st)
-              : launch_stream<MODE_GATEUP, false>(g, nseg, st);
-  else
-    err = bm1 == 256 ? launch_gemm_dt<MODE_GATEUP, 256>(g, fp8, st)
-                     : launch_gemm_dt<MODE_GATEUP, 128>(g, fp8, st);
+  hipError_t err = fp8 ? launch_gemm_dma<MODE_GATEUP, true>(g, st)
+                       : launch_gemm_dma<MODE_GATEUP, false>(g, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {
     err = hipEventRecord(ev_mid, st);
@@ -1290,9 +910,9 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.y_perm = y_perm;
   g2.K = s.d_ff;
   g2.N = s.d;
-  const int bn2 = 65536 / bm2;  // output columns per down tile
+  const int bn2 = 256;  // output columns per down tile
   g2.nt = (s.d + bn2 - 1) / bn2;
-  g2.mt_max = (int)mt_bound(bm2);
+  g2.mt_max = (int)mt_bound;
   // The tiles of the last, partial round of the schedule may be split over K
   // (pieces of at least 8 steps): with the atomic combine the partial sums
   // add up in y; with the grouped output they go to the tail slab and a
@@ -1301,23 +921,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.split_max = (y || s.d_ff >= 4096) ? std::max(1, s.d_ff / BK / 8) : 1;
   g2.tail_slab = tail_slab;
   g2.tail_cap = tail_cap;
-  if (stream_down) {
-    // K pieces so that about 8192 waves stream W2 (each at least 16 steps)
-    const int64_t waves = (int64_t)nseg * ((s.d + 63) / 64) * 4;
-    int ks = (int)std::min<int64_t>(8, (8192 + waves - 1) / waves);
-    ks = std::max(1, std::min(ks, s.d_ff / 32 / 16));
-    g2.split_max = y ? ks : 1;
-    if (y)
-      return fp8 ? launch_stream<MODE_DOWN, true>(g2, nseg, st)
-                 : launch_stream<MODE_DOWN, false>(g2, nseg, st);
-    return fp8 ? launch_stream<MODE_DOWN_PERM, true>(g2, nseg, st)
-               : launch_stream<MODE_DOWN_PERM, false>(g2, nseg, st);
-  }
   if (y)
-    return bm2 == 256 ? launch_gemm_dt<MODE_DOWN, 256>(g2, fp8, st)
-                      : launch_gemm_dt<MODE_DOWN, 128>(g2, fp8, st);
-  return bm2 == 256 ? launch_gemm_dt<MODE_DOWN_PERM, 256>(g2, fp8, st)
-                    : launch_gemm_dt<MODE_DOWN_PERM, 128>(g2, fp8, st);
+    return fp8 ? launch_gemm_dma<MODE_DOWN, true>(g2, st) : launch_gemm_dma<MODE_DOWN, false>(g2, st);
+  return fp8 ? launch_gemm_dma<MODE_DOWN_PERM, true>(g2, st)
+             : launch_gemm_dma<MODE_DOWN_PERM, false>(g2, st);
 }
 
 hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm,

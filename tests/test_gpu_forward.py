@@ -34,8 +34,8 @@ SMALL = [
     (129, 768, 32, 8, 256, 0.5, True, "bf16", None),
     (500, 256, 8, 2, 256, None, True, "fp8_e4m3", None),
     (64, 512, 8, 2, 1408, None, False, "bf16", None),
-    # few rows per expert (the weight-streaming kernels): fp8, a shared
-    # expert that takes several 32-row passes, and a capacity limit
+    # few rows per expert (mostly empty row tiles, per-wave granule counts):
+    # fp8, a shared expert over all tokens, and a capacity limit
     (64, 512, 8, 2, 1408, None, False, "fp8_e4m3", None),
     (48, 256, 4, 2, 256, None, True, "bf16", None),
     (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5"),
@@ -73,9 +73,8 @@ def test_tiny_page_layer(moe):
 @pytest.mark.parametrize("T,seed,shared", [(600, 5, False), (64, 6, False), (200, 7, True)])
 def test_unfused_path_matches_fused(moe, monkeypatch, T, seed, shared):
     """moe_expert_ffn into a grouped output, then moe_combine, against the
-    fused scatter-add path and the oracle (600 tokens: tiled GEMMs; 64:
-    the weight-streaming kernels; 200 with a shared expert, whose rows follow
-    the grouped rows)."""
+    fused scatter-add path and the oracle (600 tokens; 64, a few rows per
+    expert; 200 with a shared expert, whose rows follow the grouped rows)."""
     monkeypatch.setenv("MOE_COMBINE", "atomic")
     cfg = custom_config(T, 256, 8, 2, 256, cf=1.0, seed=seed, shared=shared)
     wl = Workload(cfg)

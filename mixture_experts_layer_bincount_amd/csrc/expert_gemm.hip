@@ -244,7 +244,7 @@ __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
   tile_place<BM>(p, s_pre, u.q, t);
   t.kbeg = __builtin_amdgcn_readfirstlane(u.kbeg * p.kunit);
   t.nk = __builtin_amdgcn_readfirstlane(u.nk * p.kunit);
-  t.slab = (MODE == MODE_DOWN_PERM && u.tail >= 0)
+  t.slab = ((MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP) && u.tail >= 0)
                ? __builtin_amdgcn_readfirstlane(xcd * p.slots + u.tail)
                : -1;
   return true;
@@ -293,6 +293,15 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
             const int gi = n / kFp8Group;
             sg = t.shared_e ? p.sc0s[gi] : p.sc0[(int64_t)t.e * (N / kFp8Group) + gi];
             su = t.shared_e ? p.sc1s[gi] : p.sc1[(int64_t)t.e * (N / kFp8Group) + gi];
+          }
+          if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
+            float* sl = p.tail_slab + (int64_t)t.slab * 65536 + (int64_t)(m - t.m0) * 256 + (n - n0);
+            *(float4*)sl = make_float4(acc[i][j][q * 4] * sg, acc[i][j][q * 4 + 1] * sg,
+                                       acc[i][j][q * 4 + 2] * sg, acc[i][j][q * 4 + 3] * sg);
+            *(float4*)(sl + 128) =
+                make_float4(acc[i][j + 2][q * 4] * su, acc[i][j + 2][q * 4 + 1] * su,
+                            acc[i][j + 2][q * 4 + 2] * su, acc[i][j + 2][q * 4 + 3] * su);
+            continue;
           }
           uint32_t hb[4];
 #pragma unroll
@@ -699,16 +708,18 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
   }
 }
 
-// Tail fixup of the grouped-output down projection: the pieces of a split
-// tail tile left fp32 partial tiles in p.tail_slab; sum them in piece order
-// and store the tile's valid rows.  kFixBands workgroups share a tile, one
-// band of rows each: workgroup b is XCD b % 8, then (tail tile, band) of
-// b / 8 (the same schedule arithmetic as the GEMM, from the same offsets).
+// Tail fixup: the pieces of a split tail tile left fp32 partial tiles in
+// p.tail_slab (GATEUP: [row][128 gate | 128 up] sums, already scaled;
+// DOWN_PERM: [row][256 outputs]); sum them in piece order and finish the
+// tile's valid rows (GATEUP: SwiGLU into H; DOWN_PERM: the grouped output).
+// kFixBands workgroups share a tile, one band of rows each: workgroup b is
+// XCD b % 8, then (tail tile, band) of b / 8 (the same schedule arithmetic
+// as the GEMM, from the same offsets).
 constexpr int kFixBands = 16;
-template <int BM>
+template <int MODE>
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
-  constexpr int BNB = 65536 / BM;
-  constexpr int BAND = 65536 / kFixBands;  // floats per band
+  constexpr int BM = DMA_BM;
+  constexpr int ROWS = BM / kFixBands;  // rows per band
   __shared__ int s_scan[4];
   __shared__ int s_pre[kMaxSegments + 1];
   const int xcd = (int)(blockIdx.x % kNumXcd);
@@ -721,29 +732,51 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   if (r >= rem || S <= 1) return;
   TileMap t;
   tile_place<BM>(p, s_pre, qtail + r, t);
-  const int n0 = t.ntile * BNB;
-  const int64_t orow0 = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
   const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * 65536;
-  constexpr int PER = BAND / 4 / 256;  // float4 per thread
-  float4 a[PER];
-  int idx[PER];
+  const int64_t obase = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
+  // ROWS x 256 floats per band: 16 rows x 64 float4 = 4 float4 per thread;
+  // GATEUP pairs the gate float4 at column c with the up float4 at c + 128
+  constexpr int NV = (MODE == MODE_GATEUP) ? 2 : 4;
+  float4 a[NV], u[NV];
+  int row[NV], col[NV];
 #pragma unroll
-  for (int v = 0; v < PER; ++v) {
-    idx[v] = band * BAND + (v * 256 + (int)threadIdx.x) * 4;
-    a[v] = *(const float4*)(slab + idx[v]);
+  for (int v = 0; v < NV; ++v) {
+    const int it = v * 256 + (int)threadIdx.x;  // GATEUP: 16 rows x 32 float4 of gate
+    row[v] = band * ROWS + (MODE == MODE_GATEUP ? it / 32 : it / 64);
+    col[v] = (MODE == MODE_GATEUP ? it % 32 : it % 64) * 4;
+    const float* src = slab + row[v] * 256 + col[v];
+    a[v] = *(const float4*)src;
+    if (MODE == MODE_GATEUP) u[v] = *(const float4*)(src + 128);
   }
   for (int pc = 1; pc < S; ++pc) {
 #pragma unroll
-    for (int v = 0; v < PER; ++v) {
-      const float4 b = *(const float4*)(slab + (int64_t)pc * 65536 + idx[v]);
+    for (int v = 0; v < NV; ++v) {
+      const float* src = slab + (int64_t)pc * 65536 + row[v] * 256 + col[v];
+      const float4 b = *(const float4*)src;
       a[v].x += b.x; a[v].y += b.y; a[v].z += b.z; a[v].w += b.w;
+      if (MODE == MODE_GATEUP) {
+        const float4 c = *(const float4*)(src + 128);
+        u[v].x += c.x; u[v].y += c.y; u[v].z += c.z; u[v].w += c.w;
+      }
     }
   }
+  const int n0 = (MODE == MODE_GATEUP) ? t.ntile * 128 : t.ntile * 256;
 #pragma unroll
-  for (int v = 0; v < PER; ++v) {
-    const int row = idx[v] / BNB, col = idx[v] % BNB;
-    if (t.m0 + row < t.rows && n0 + col < p.N)
-      *(float4*)(p.y_perm + (orow0 + row) * p.N + n0 + col) = a[v];
+  for (int v = 0; v < NV; ++v) {
+    if (t.m0 + row[v] >= t.rows || n0 + col[v] >= p.N) continue;
+    if (MODE == MODE_GATEUP) {
+      const float g[4] = {a[v].x, a[v].y, a[v].z, a[v].w};
+      const float up[4] = {u[v].x, u[v].y, u[v].z, u[v].w};
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16_bits(g[q] / (1.f + __expf(-g[q])) * up[q]);
+      uint2 w;
+      w.x = hb[0] | (hb[1] << 16);
+      w.y = hb[2] | (hb[3] << 16);
+      *(uint2*)(p.H + (obase + row[v]) * p.N + n0 + col[v]) = w;
+    } else {
+      *(float4*)(p.y_perm + (obase + row[v]) * p.N + n0 + col[v]) = a[v];
+    }
   }
 }
 
@@ -824,10 +857,11 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
-  if (MODE == MODE_DOWN_PERM && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
+  constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
+  if (slab_mode && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
   grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8><<<sched_grid(p), 256, C::LDS, st>>>(p);
-  if (MODE == MODE_DOWN_PERM && p.split_max > 1)
-    tail_fixup_kernel<DMA_BM><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
+  if (slab_mode && p.split_max > 1)
+    tail_fixup_kernel<MODE><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -871,7 +905,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.E = s.E;
   g.has_shared = has_sh;
   g.mt_max = (int)mt_bound;
-  g.split_max = 1;
+  g.tail_slab = tail_slab;
+  g.tail_cap = tail_cap;
   {
     const char* kr = getenv("MOE_GEMM_KROT");
     const char* ax = getenv("MOE_GEMM_AUX");
@@ -891,6 +926,9 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.N = s.d_ff;
   const int bn1 = 128;  // hidden columns per gate/up tile (128 of W1 + 128 of W3)
   g.nt = (s.d_ff + bn1 - 1) / bn1;
+  // tail tiles split over K through the slab + fixup (SwiGLU needs whole
+  // sums), for long K loops only, as in the down projection
+  g.split_max = s.d >= 4096 ? std::max(1, s.d / BK / 8) : 1;
   hipError_t err = fp8 ? launch_gemm_dma<MODE_GATEUP, true>(g, st)
                        : launch_gemm_dma<MODE_GATEUP, false>(g, st);
   if (err != hipSuccess) return err;

@@ -46,6 +46,10 @@ SMALL = [
     # tail tile summed by the fixup pass (grouped output), bf16 and fp8
     (600, 512, 4, 2, 4096, None, True, "bf16", None),
     (600, 512, 4, 2, 4096, None, False, "fp8_e4m3", None),
+    # long gate/up K (d = 4096) with few tiles: every gate/up tile is split,
+    # its gate and up partial sums finished (SwiGLU) by the fixup pass
+    (300, 4096, 4, 2, 256, None, True, "bf16", None),
+    (300, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
 ]
 
 

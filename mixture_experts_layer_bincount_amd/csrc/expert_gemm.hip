@@ -590,8 +590,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   auto run = [&](auto NGc) __attribute__((always_inline)) {
     constexpr int NG = decltype(NGc)::value;
     constexpr int NGA = NG > 0 ? NG : 1;
-    bf16x8 fa0[2][NGA], fb0[2][4], fa1[2][NGA], fb1[2][4];
-    auto read_slice = [&](int sl, bf16x8 (&fa)[2][NGA], bf16x8 (&fb)[2][4]) __attribute__((always_inline)) {
+    // weight fragments: bf16, or the raw fp8 codes, widened just before their
+    // MFMAs (so the LDS reads of the next slice need not land early)
+    using BFrag = std::conditional_t<FP8, uint2, bf16x8>;
+    bf16x8 fa0[2][NGA], fa1[2][NGA];
+    BFrag fb0[2][4], fb1[2][4];
+    auto read_slice = [&](int sl, bf16x8 (&fa)[2][NGA], BFrag (&fb)[2][4]) __attribute__((always_inline)) {
       if constexpr (NG > 0) {
         const int stage = (sl / HPS) % NS;
         const int h = sl % HPS;
@@ -608,8 +612,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           } else {
             const int cb = ((h * 2 + kk) ^ swzb) * 16 + fhalf * 8;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              fb[kk][j] = fp8x8_to_bf16x8(*(const uint2*)(b + (brow[j] + frow) * C::RBB + cb));
+            for (int j = 0; j < 4; ++j) fb[kk][j] = *(const uint2*)(b + (brow[j] + frow) * C::RBB + cb);
           }
         });
       }
@@ -617,20 +620,34 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     // MFMAs of one slice from (fa, fb) with the reads of slice `next` into
     // (ga, gb) interleaved.  `next` may be past the end: it then rereads a
     // valid stage and the values go unused.
-    auto slice = [&](bf16x8 (&fa)[2][NGA], bf16x8 (&fb)[2][4], int next, bf16x8 (&ga)[2][NGA],
-                     bf16x8 (&gb)[2][4]) __attribute__((always_inline)) {
+    auto slice = [&](bf16x8 (&fa)[2][NGA], BFrag (&fb)[2][4], int next, bf16x8 (&ga)[2][NGA],
+                     BFrag (&gb)[2][4]) __attribute__((always_inline)) {
       if constexpr (NG > 0) {
         read_slice(next < nsl ? next : nsl - 1, ga, gb);
         static_for<2>([&](auto kk) {
+          if constexpr (!FP8) {
 #pragma unroll
-          for (int i = 0; i < NG; ++i)
+            for (int i = 0; i < NG; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                if (MODE == MODE_GATEUP)
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+                else
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+              }
+          } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              if (MODE == MODE_GATEUP)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+              const bf16x8 bv = fp8x8_to_bf16x8(fb[kk][j]);
+#pragma unroll
+              for (int i = 0; i < NG; ++i) {
+                if (MODE == MODE_GATEUP)
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, fa[kk][i], acc[i][j], 0, 0, 0);
+                else
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], bv, acc[i][j], 0, 0, 0);
+              }
             }
+          }
         });
         constexpr int NR = 2 * (NG + 4), NM = 8 * NG, MPR = (NM + NR - 1) / NR;
         static_for<NR>([&](auto) {

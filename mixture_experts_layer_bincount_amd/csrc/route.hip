@@ -104,22 +104,27 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
-// One wave: 64 token rows x 16*NJ experts (16x16x32 MFMA tiles); a workgroup
-// of 4 waves covers 256 rows.  Operand fragments (16 bytes per lane: row
-// lane%16, K chunk lane/16) are read straight from global memory; the
+// Workgroup of 4 waves: WE waves along the experts (each 16*NJ of them) and
+// 4/WE along the tokens (64 rows each), so a wave's tile stays small enough
+// to double-buffer its operand fragments.  Fragments (16 bytes per lane: row
+// lane%16, K chunk lane/16) are read straight from global memory, the next
+// 32-deep step's while the current step's 16x16x32 MFMAs run; the
 // workgroup's K range is one split of the reduction.
-template <int NJ>
+template <int NJ, int WE>
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ Wp,
                                                           float* __restrict__ partial, int64_t T,
                                                           int d, int E, int E_pad, int ksteps_per) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  constexpr int WM = 4 / WE;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  const int we = wave % WE, wm = wave / WE;
+  const int64_t r0 = (int64_t)blockIdx.x * (64 * WM) + wm * 64;
+  const int e0 = we * NJ * 16;
   const int split = blockIdx.y;
   const int k0 = split * ksteps_per * 32;
-  const int k1 = min(d, k0 + ksteps_per * 32);
+  const int k1 = min(d, k0 + ksteps_per * 32);  // an empty last split stores zeros
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const uint16_t* arow[4];
 #pragma unroll
@@ -128,27 +133,45 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     arow[i] = x + t * d + fk;
   }
   const int64_t plane = (int64_t)E_pad * d;
+  const uint16_t* brow = Wp + (int64_t)(e0 + fr) * d + fk;
   f32x4 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = k0; k < k1; k += 32) {
-    bf16x8_t a[4];
+  auto load = [&](int k, bf16x8_t (&a)[4], bf16x8_t (&b)[3][NJ]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(arow[i] + k);
 #pragma unroll
-    for (int part = 0; part < 3; ++part) {
+    for (int part = 0; part < 3; ++part)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const bf16x8_t b = *(const bf16x8_t*)(Wp + part * plane + (int64_t)(j * 16 + fr) * d + k + fk);
+      for (int j = 0; j < NJ; ++j)
+        b[part][j] = *(const bf16x8_t*)(brow + part * plane + (int64_t)j * 16 * d + k);
+  };
+  auto mma = [&](bf16x8_t (&a)[4], bf16x8_t (&b)[3][NJ]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[part][j], acc[i][j], 0, 0, 0);
+  };
+  // two steps per iteration, fragments of the next step loaded under the
+  // current one's MFMAs (a reload past the end rereads the last step, unused)
+  if (k0 < k1) {
+    bf16x8_t a0[4], b0[3][NJ], a1[4], b1[3][NJ];
+    load(k0, a0, b0);
+    int k = k0;
+    for (; k + 64 <= k1; k += 64) {
+      load(k + 32, a1, b1);
+      mma(a0, b0);
+      load(min(k + 64, k1 - 32), a0, b0);
+      mma(a1, b1);
     }
+    if (k < k1) mma(a0, b0);
   }
-  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert j*16 + lane%16
+  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert e0 + j*16 + lane%16
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -157,7 +180,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       if (t >= T) continue;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int e = j * 16 + fr;
+        const int e = e0 + j * 16 + fr;
         if (e < E) partial[((int64_t)split * T + t) * E + e] = acc[i][j][r];
       }
     }
@@ -271,13 +294,19 @@ size_t router_split_bytes(const moe_shape& s) {
   return ep ? (size_t)3 * ep * s.d * sizeof(uint16_t) : 0;
 }
 
+// Waves along the experts in the MFMA router: as many as 16-expert tiles
+// allow, up to the workgroup's 4.
+static int router_we(int ep) { return std::min(4, ep / 16); }
+
 int router_splits_for(const moe_shape& s) {
-  if (router_mfma_epad(s)) {
-    const int64_t wgs = (s.T + 255) / 256;
+  const int ep = router_mfma_epad(s);
+  if (ep) {
+    // about 512 workgroups (2048 waves), K pieces of at least 8 steps of 32
+    const int rows_per_wg = 64 * (4 / router_we(ep));
+    const int64_t wgs = std::max<int64_t>(1, (s.T + rows_per_wg - 1) / rows_per_wg);  // T may be 0
     const int ksteps = s.d / 32;
-    int sp = 1;
-    while (wgs * sp < 256 && ksteps / (sp * 2) >= 4) sp *= 2;
-    return sp;
+    const int64_t want = (512 + wgs - 1) / wgs;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, ksteps / 8)));
   }
   const int64_t mt = (s.T + 63) / 64;
   const int kmax = std::max(1, (s.d + 63) / 64);
@@ -294,14 +323,15 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_
         W_g, s.d, s.E, ep, Wp);
     const int ksteps = s.d / 32;
     const int per = (ksteps + splits - 1) / splits;
-    dim3 grid((unsigned)((s.T + 255) / 256), (unsigned)splits);
-#define MOE_RM(NJ)                                                                           \
-  if (ep == NJ * 16) {                                                                       \
-    router_mfma_kernel<NJ><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d, \
-                                                 s.E, ep, per);                              \
-    return hipGetLastError();                                                                \
+    const int rows_per_wg = 64 * (4 / router_we(ep));
+    dim3 grid((unsigned)((s.T + rows_per_wg - 1) / rows_per_wg), (unsigned)splits);
+#define MOE_RM(EP, NJ, WE)                                                                        \
+  if (ep == EP) {                                                                                 \
+    router_mfma_kernel<NJ, WE><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d,   \
+                                                     s.E, ep, per);                               \
+    return hipGetLastError();                                                                     \
   }
-    MOE_RM(1) MOE_RM(2) MOE_RM(4) MOE_RM(8) MOE_RM(16)
+    MOE_RM(16, 1, 1) MOE_RM(32, 1, 2) MOE_RM(64, 1, 4) MOE_RM(128, 2, 4) MOE_RM(256, 4, 4)
 #undef MOE_RM
     return hipErrorInvalidValue;
   }

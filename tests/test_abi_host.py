@@ -66,6 +66,15 @@ def test_workspace_bytes(moe):
     assert moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 0, 2, 14336)) == 0
 
 
+@pytest.mark.parametrize("T,d,E,k", [(0, 256, 8, 2), (0, 4096, 256, 8), (1, 4160, 128, 4),
+                                     (0, 8, 4, 2)])
+def test_workspace_bytes_degenerate(moe, T, d, E, k):
+    """The workspace layout (router splits, slab, grouped output) is computed
+    on the host for any valid shape, T = 0 included, without faulting."""
+    s = moe.make_shape(T, d, E, k, 128)
+    assert moe.moe_workspace_bytes(s) >= 0
+
+
 @pytest.mark.parametrize("kw,needle", [
     (dict(T=-1), "T="), (dict(E=0), "E="), (dict(top_k=9), "top_k"), (dict(top_k=0), "top_k"),
     (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 64"),

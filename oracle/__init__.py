@@ -16,9 +16,13 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
   bincount             pinned (sum = T*k, tutorial §3.2 total, brute force)
   capacity             pinned (definition bounds, tutorial Q2 example, skew workload value)
   capacity_ranks / dispatch   pinned (tutorial Q2 example, brute-force invariants)
+  reroute              pinned (hand-worked examples in tests/golden, zero rounds
+                       = drop, unlimited capacity = no-op, capacity / distinctness
+                       / exhaustion invariants, a per-expert queue re-statement)
   expert_linear_bias / expert_swiglu   pinned (closed forms)
   forward              pinned (MOE 学习笔记 combine example, dense brute force,
-                       identical-expert identity, C=0 / shared-only case)
+                       identical-expert identity, C=0 / shared-only case,
+                       overflow-to-shared closed form)
   stats (imbalance, LPT, naive split, variance)   pinned (tutorial §3.3 / §6 values,
                        4/3 bound against brute-force OPT)
   fp8 e4m3 decode      pinned (OCP format values, torch float8_e4m3fn)
@@ -27,7 +31,7 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
 """
 from .moe_oracle import (  # noqa: F401
     widen, router_logits, select_topk, route, route_softmax_of_topk,
-    bincount, capacity, capacity_ranks, dispatch, silu, expert_linear_bias,
+    bincount, capacity, capacity_ranks, dispatch, reroute, silu, expert_linear_bias,
     expert_swiglu, forward, forward_tokens, dense_forward, topk_margin,
 )
 from .stats import expert_imbalance, lpt_pack, naive_split, sample_variance  # noqa: F401

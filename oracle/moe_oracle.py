@@ -14,6 +14,15 @@ give it:
               dropped and add nothing (their token keeps the residual path)
                                                 fde-learning "MoE 并行", Capacity
                                                 Factor; tutorial Q2
+  overflow    instead of dropping (a policy, "drop" by default):
+              "reroute": in rounds, every dropped assignment moves to its
+              token's next-ranked unused expert; an expert accepts the round's
+              requests in token order while it has capacity left
+                                                fde-learning "MoE 并行", 推理时
+                                                的负载均衡 (dynamic re-routing)
+              "shared": a dropped assignment's weight goes to the shared
+              expert                            tutorial Q2 (overflow to the
+                                                shared expert)
   experts     for e in experts: mask = (topk_idx == e) & kept;
               out[mask] += w * expert_e(x[mask])  tutorial §3.1 diagram
   shared      y += shared_expert(x) for every token, weight 1
@@ -137,13 +146,17 @@ def capacity(T: int, E: int, k: int, cf) -> int:
 
 def capacity_ranks(idx: np.ndarray, E: int) -> np.ndarray:
     """rank[t, j]: how many earlier tokens t' < t also chose expert idx[t, j].
-    A plain walk in token order; a token never picks one expert twice."""
+    A plain walk in token order; a token never picks one expert twice.
+    Entries -1 (no expert) get rank -1 and are not counted."""
     T, k = idx.shape
     seen = np.zeros(E, dtype=np.int64)
     rank = np.empty((T, k), dtype=np.int64)
     for t in range(T):
         for j in range(k):
             e = int(idx[t, j])
+            if e < 0:
+                rank[t, j] = -1
+                continue
             rank[t, j] = seen[e]
             seen[e] += 1
     return rank
@@ -156,15 +169,16 @@ def dispatch(idx: np.ndarray, w: np.ndarray, E: int, C: int):
     of kept), keep[T,k] bool, rank[T,k], perm_token[P], perm_slot[P],
     perm_w[P] and slot_pos[T,k] (position in the grouped order, -1 if
     dropped).  Dropped assignments add nothing (tutorial Q2: overflow is
-    dropped; fde-learning: overflow takes the residual path)."""
+    dropped; fde-learning: overflow takes the residual path).  idx entries -1
+    stand for assignments already dropped (no expert)."""
     T, k = idx.shape
-    counts = bincount(idx, E)
+    counts = bincount(idx[idx >= 0], E)
     rank = capacity_ranks(idx, E)
     if C < 0:
-        keep = np.ones((T, k), dtype=bool)
+        keep = idx >= 0
         kept = counts.copy()
     else:
-        keep = rank < C
+        keep = (idx >= 0) & (rank < C)
         kept = np.minimum(counts, C)
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(kept)
@@ -185,6 +199,42 @@ def dispatch(idx: np.ndarray, w: np.ndarray, E: int, C: int):
     return dict(counts=counts, kept=kept, offsets=offsets, keep=keep, rank=rank,
                 perm_token=perm_token, perm_slot=perm_slot, perm_w=perm_w,
                 slot_pos=slot_pos, C=C)
+
+
+def reroute(logits: np.ndarray, idx: np.ndarray, E: int, C: int, rounds: int) -> np.ndarray:
+    """Overflow re-routing: the final expert of every (token, slot), -1 for an
+    assignment that stays dropped.
+
+    fde-learning "MoE 并行" (推理时的负载均衡): when an expert is over its
+    capacity, the token is routed to the next expert.  Read here as rounds:
+    the first pass keeps, per expert, the first C assignments in token order
+    (as dispatch()); then in each round every still-dropped assignment, taken
+    in token order and slot order, requests its token's next ranked expert
+    that the token has not used or requested yet (ranks by logit, ties to the
+    lower index, as select_topk), and each expert accepts requests in that
+    order while it has capacity left.  Requests that find the expert full
+    wait for the next round.  After `rounds` rounds the rest are dropped."""
+    T, k = idx.shape
+    if C < 0:
+        return np.asarray(idx, dtype=np.int64).copy()
+    ranked = select_topk(logits, E)
+    rank = capacity_ranks(idx, E)
+    final = np.where(rank < C, idx, -2).astype(np.int64)  # -2: waiting
+    used = np.minimum(bincount(idx, E), C)
+    nxt = np.full(T, k, dtype=np.int64)  # next unused position in ranked[t]
+    for _ in range(rounds):
+        requests = []
+        for t in range(T):
+            for j in range(k):
+                if final[t, j] == -2 and nxt[t] < E:
+                    requests.append((t, j, int(ranked[t, nxt[t]])))
+                    nxt[t] += 1
+        for t, j, e in requests:
+            if used[e] < C:
+                final[t, j] = e
+                used[e] += 1
+    final[final == -2] = -1
+    return final
 
 
 # ---------------------------------------------------------------- experts
@@ -215,7 +265,7 @@ def _expert_fn(kind: str):
 
 # ---------------------------------------------------------------- layer
 def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
-            idx_override=None, logits=None):
+            idx_override=None, logits=None, overflow="drop", rounds=0):
     """The whole layer, masked loop over experts (tutorial §3.1).
 
     expert(e) -> dict of that expert's weights; shared() -> dict or None.
@@ -223,7 +273,13 @@ def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
     top-k margin is too small for the selection to be unique in fp32); the
     weights are then those of the given selection.
 
-    Returns a dict with logits, idx, w, the dispatch fields and y[T, d]
+    overflow: "drop" (dropped assignments add nothing), "reroute" (reroute()
+    with `rounds` rounds; an assignment keeps its weight at its new expert)
+    or "shared" (the dropped weights are added to the shared expert's weight
+    of 1).
+
+    Returns a dict with logits, idx, w, final (the expert each assignment
+    ends at, -1 dropped), the dispatch fields of `final` and y[T, d]
     (float64; the MoE branch only: the residual is the caller's)."""
     if logits is None:
         logits = router_logits(x, W_g, b_g)
@@ -232,29 +288,52 @@ def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
     else:
         idx = np.asarray(idx_override, dtype=np.int32)
         w = weights_for(logits, idx)
-    dsp = dispatch(idx, w, E, C)
+    final = _final_assignment(logits, idx, E, C, overflow, rounds)
+    dsp = dispatch(final, w, E, -1)
+    dsp["counts"] = bincount(idx, E)  # the router's loads, before capacity
+    dsp["C"] = C
     X = widen(x)
     T, d = X.shape
     y = np.zeros((T, d), dtype=np.float64)
     f = _expert_fn(kind)
     for e in range(E):
-        mask = (idx == e) & dsp["keep"]
+        mask = final == e
         t_rows, j_rows = np.nonzero(mask)
         if t_rows.size == 0:
             continue
         Y = f(X[t_rows], expert(e))
-        y[t_rows] += w[t_rows, j_rows][:, None] * Y  # a token picks e at most once
+        y[t_rows] += w[t_rows, j_rows][:, None] * Y  # a token reaches e at most once
     if shared is not None:
         sw = shared()
         if sw is not None:
-            y += expert_swiglu(X, sw)
-    out = dict(logits=logits, idx=idx, w=w, y=y)
+            y += _shared_weight(w, final, overflow)[:, None] * expert_swiglu(X, sw)
+    out = dict(logits=logits, idx=idx, w=w, final=final, y=y)
     out.update(dsp)
     return out
 
 
+def _final_assignment(logits, idx, E, C, overflow, rounds):
+    """The expert each (token, slot) ends at under the overflow policy."""
+    if overflow == "reroute":
+        return reroute(logits, idx, E, C, rounds)
+    if overflow not in ("drop", "shared"):
+        raise ValueError(f"overflow policy {overflow!r}")
+    if C < 0:
+        return np.asarray(idx, dtype=np.int64).copy()
+    return np.where(capacity_ranks(idx, E) < C, idx, -1).astype(np.int64)
+
+
+def _shared_weight(w, final, overflow):
+    """Weight of the shared expert per token: 1, plus the dropped assignments'
+    weights under the "shared" policy (tutorial Q2)."""
+    sw = np.ones(w.shape[0], dtype=np.float64)
+    if overflow == "shared":
+        sw += np.where(final < 0, w, 0.0).sum(axis=1)
+    return sw
+
+
 def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
-                   shared=None, idx_override=None):
+                   shared=None, idx_override=None, overflow="drop", rounds=0):
     """The same layer evaluated only at the given tokens.
 
     Routing, counts and capacity ranks are computed for all T tokens (a
@@ -268,42 +347,53 @@ def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
     else:
         idx = np.asarray(idx_override, dtype=np.int32)
         w = weights_for(logits, idx)
-    dsp = dispatch(idx, w, E, C)
+    final = _final_assignment(logits, idx, E, C, overflow, rounds)
+    dsp = dispatch(final, w, E, -1)
+    dsp["counts"] = bincount(idx, E)
+    dsp["C"] = C
     tokens = np.asarray(tokens, dtype=np.int64)
     X = widen(x[tokens])
     y = np.zeros((tokens.size, X.shape[1]), dtype=np.float64)
     f = _expert_fn(kind)
-    sel_idx = idx[tokens]
-    sel_keep = dsp["keep"][tokens]
+    sel_final = final[tokens]
     sel_w = w[tokens]
-    for e in np.unique(sel_idx[sel_keep]):
-        r, j = np.nonzero((sel_idx == e) & sel_keep)
+    for e in np.unique(sel_final[sel_final >= 0]):
+        r, j = np.nonzero(sel_final == e)
         Y = f(X[r], expert(int(e)))
         y[r] += sel_w[r, j][:, None] * Y
     if shared is not None:
         sw = shared()
         if sw is not None:
-            y += expert_swiglu(X, sw)
-    out = dict(logits=logits, idx=idx, w=w)
+            y += _shared_weight(sel_w, sel_final, overflow)[:, None] * expert_swiglu(X, sw)
+    out = dict(logits=logits, idx=idx, w=w, final=final)
     out.update(dsp)
     return y, out
 
 
-def dense_forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None):
+def dense_forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
+                  overflow="drop", rounds=0):
     """Brute force for tiny inputs: run every expert on every token, then sum
     over all experts with a dense [T, E] weight that is w[t, j] where expert e
-    is token t's kept j-th choice and 0 elsewhere (the sum-over-all-experts
-    form of the iopenshare §1.2 Switch layer, weighted).  Must equal forward()."""
+    is where token t's j-th choice ends (kept, or re-routed) and 0 elsewhere
+    (the sum-over-all-experts form of the iopenshare §1.2 Switch layer,
+    weighted); the shared expert's weight is 1 plus, under the "shared"
+    policy, every weight left without an expert.  Must equal forward()."""
     logits = router_logits(x, W_g, b_g)
     idx, w = route(logits, k)
     T = idx.shape[0]
-    rank = capacity_ranks(idx, E)
-    keep = np.ones_like(rank, dtype=bool) if C < 0 else rank < C
+    if overflow == "reroute":
+        dest = reroute(logits, idx, E, C, rounds)
+    else:
+        rank = capacity_ranks(idx, E)
+        dest = np.where((C < 0) | (rank < C), idx, -1)
     Wd = np.zeros((T, E), dtype=np.float64)
+    Ws = np.ones(T, dtype=np.float64)
     for t in range(T):
         for j in range(k):
-            if keep[t, j]:
-                Wd[t, idx[t, j]] = w[t, j]
+            if dest[t, j] >= 0:
+                Wd[t, dest[t, j]] = w[t, j]
+            elif overflow == "shared":
+                Ws[t] += w[t, j]
     X = widen(x)
     f = _expert_fn(kind)
     y = np.zeros_like(X)
@@ -312,5 +402,5 @@ def dense_forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None
     if shared is not None:
         sw = shared()
         if sw is not None:
-            y += expert_swiglu(X, sw)
+            y += Ws[:, None] * expert_swiglu(X, sw)
     return y

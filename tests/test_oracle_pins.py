@@ -342,6 +342,134 @@ def test_topk_margin():
     assert oracle.topk_margin(l, 4)[0] == 0.5          # k = E: last gap skipped
 
 
+# ------------------------------------------------------------------ f1: overflow policies
+def test_reroute_hand_worked_examples():
+    g = _golden("reroute_examples.json")
+    for c in g["cases"]:
+        logits = np.array(c["logits"], np.float32)
+        idx, _ = oracle.route(logits, c["k"])
+        got = oracle.reroute(logits, idx, c["E"], c["C"], c["rounds"])
+        assert got.tolist() == c["expected"], c["name"]
+
+
+def _reroute_by_queues(logits, idx, E, C, rounds):
+    """The same re-routing stated per expert: each round every expert takes the
+    queue of requests addressed to it, ordered by (token, slot), and admits the
+    head of the queue up to its free room.  Preference lists come from a plain
+    Python sort on (-logit, expert)."""
+    T, k = idx.shape
+    pref = [sorted(range(E), key=lambda e: (-float(logits[t, e]), e)) for t in range(T)]
+    dest = {}
+    room = {e: C for e in range(E)}
+    for e in range(E):
+        queue = sorted((t, j) for t in range(T) for j in range(k) if idx[t, j] == e)
+        for t, j in queue[:C]:
+            dest[(t, j)] = e
+        room[e] = C - min(C, len(queue))
+    asked = {t: set(int(v) for v in idx[t]) for t in range(T)}
+    for _ in range(rounds):
+        queues = {e: [] for e in range(E)}
+        for t in range(T):
+            for j in range(k):
+                if (t, j) in dest:
+                    continue
+                left = [e for e in pref[t] if e not in asked[t]]
+                if left:
+                    asked[t].add(left[0])
+                    queues[left[0]].append((t, j))
+        for e, q in queues.items():
+            for t, j in sorted(q)[:room[e]]:
+                dest[(t, j)] = e
+            room[e] -= min(room[e], len(q))
+    return np.array([[dest.get((t, j), -1) for j in range(k)] for t in range(T)])
+
+
+@pytest.mark.parametrize("T,E,k,C,rounds,skew", [
+    (40, 4, 1, 8, 1, 1.5), (40, 4, 1, 8, 3, 1.5), (60, 8, 2, 10, 2, 2.0),
+    (50, 6, 3, 20, 4, 1.0), (30, 5, 2, 3, 5, 3.0), (64, 16, 4, 12, 2, 2.5)])
+def test_reroute_equals_queue_restatement_and_invariants(T, E, k, C, rounds, skew):
+    rng = np.random.default_rng(T * 31 + E * 7 + rounds)
+    logits = rng.integers(-4, 5, size=(T, E)).astype(np.float32)   # many ties
+    logits[:, 0] += skew
+    idx, _ = oracle.route(logits, k)
+    fin = oracle.reroute(logits, idx, E, C, rounds)
+    assert np.array_equal(fin, _reroute_by_queues(logits, idx, E, C, rounds))
+    # capacity respected, experts distinct per token, first-pass keeps unchanged
+    assert np.all(np.bincount(fin[fin >= 0], minlength=E) <= C)
+    for t in range(T):
+        got = fin[t][fin[t] >= 0]
+        assert len(set(got.tolist())) == got.size
+    first = oracle.dispatch(idx, np.ones(idx.shape), E, C)["keep"]
+    assert np.array_equal(fin[first], idx[first])
+    # a moved slot lands on an expert outside the token's own top-k
+    moved = (fin >= 0) & ~first
+    for t, j in zip(*np.nonzero(moved)):
+        assert fin[t, j] not in idx[t]
+    # more rounds only add: every placement of `rounds` survives in `rounds + 1`
+    more = oracle.reroute(logits, idx, E, C, rounds + 1)
+    assert np.all(more[fin >= 0] == fin[fin >= 0])
+    assert (more >= 0).sum() >= (fin >= 0).sum()
+
+
+def test_reroute_closed_forms():
+    rng = np.random.default_rng(41)
+    logits = rng.standard_normal((80, 8)).astype(np.float32)
+    logits[:, 2] += 2.0
+    idx, _ = oracle.route(logits, 2)
+    C = 12
+    drop = oracle.dispatch(idx, np.ones(idx.shape), 8, C)["keep"]
+    assert np.array_equal(oracle.reroute(logits, idx, 8, C, 0), np.where(drop, idx, -1))
+    big = int(np.bincount(idx.ravel()).max())
+    assert np.array_equal(oracle.reroute(logits, idx, 8, big, 3), idx)
+    assert np.array_equal(oracle.reroute(logits, idx, 8, -1, 3), idx)
+    # C = 0: nothing can be placed however many rounds
+    assert np.all(oracle.reroute(logits, idx, 8, 0, 6) == -1)
+    # enough rounds: a slot stays dropped only if every expert its token does
+    # not hold is full
+    fin = oracle.reroute(logits, idx, 8, C, 8 - 2)
+    load = np.bincount(fin[fin >= 0], minlength=8)
+    for t, j in zip(*np.nonzero(fin < 0)):
+        others = [e for e in range(8) if e not in fin[t]]
+        assert all(load[e] == C for e in others)
+    # re-routing never loses a first-pass keep
+    assert (fin >= 0).sum() >= drop.sum()
+
+
+@pytest.mark.parametrize("overflow,rounds", [("drop", 0), ("reroute", 1), ("reroute", 3),
+                                             ("shared", 0)])
+@pytest.mark.parametrize("T,d,E,k,d_ff,C", [(40, 8, 4, 2, 12, 9), (33, 6, 8, 3, 10, 7),
+                                            (25, 4, 5, 1, 3, 4)])
+def test_overflow_policies_equal_dense_brute_force(overflow, rounds, T, d, E, k, d_ff, C):
+    x, W_g, ex, sh = _tiny_swiglu(T, d, E, d_ff, seed=T * 5 + E, shared=True)
+    b = np.linspace(1.0, -1.0, E).astype(np.float32)     # skew so the capacity binds
+    kw = dict(C=C, shared=lambda: sh, overflow=overflow, rounds=rounds)
+    r = oracle.forward(x, W_g, b, k, E, lambda e: ex[e], **kw)
+    yd = oracle.dense_forward(x, W_g, b, k, E, lambda e: ex[e], **kw)
+    np.testing.assert_allclose(r["y"], yd, rtol=0, atol=1e-12)
+    toks = [0, T // 2, T - 1]
+    yr, _ = oracle.forward_tokens(toks, x, W_g, b, k, E, lambda e: ex[e], **kw)
+    np.testing.assert_allclose(yr, r["y"][toks], rtol=0, atol=1e-12)
+
+
+def test_overflow_to_shared_closed_forms():
+    x, W_g, ex, sh = _tiny_swiglu(20, 8, 4, 8, seed=13, shared=True)
+    X = x.astype(np.float64)
+    # C = 0: every routed weight goes to the shared expert, and they sum to 1
+    r = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=0, shared=lambda: sh,
+                       overflow="shared")
+    np.testing.assert_allclose(r["y"], 2.0 * oracle.expert_swiglu(X, sh), rtol=1e-14, atol=1e-14)
+    # nothing dropped: the same as the plain layer
+    a = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], shared=lambda: sh, overflow="shared")
+    b = oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], shared=lambda: sh)
+    assert np.array_equal(a["y"], b["y"])
+    # identical routed and shared experts: y = 2 * expert(x) whatever is dropped
+    r2 = oracle.forward(x, W_g, None, 2, 4, lambda e: sh, C=3, shared=lambda: sh,
+                        overflow="shared")
+    np.testing.assert_allclose(r2["y"], 2.0 * oracle.expert_swiglu(X, sh), rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.forward(x, W_g, None, 2, 4, lambda e: ex[e], C=3, overflow="spill")
+
+
 # ------------------------------------------------------------------ a9: load stats
 def test_lpt_page_example():
     g = _golden("lpt_example.json")

@@ -6,6 +6,7 @@
  * compute -> gather -> weighted combine; adv12 MoE + EPLB tutorial §3.1):
  *
  *   moe_route       router Linear, softmax, top-k, renormalised weights
+ *   moe_reroute     (optional) overflow re-routing of over-capacity assignments
  *   moe_dispatch    per-expert bincount, exclusive-scan offsets, capacity drop,
  *                   grouping permutation (and optionally the gathered rows)
  *   moe_expert_ffn  grouped expert FFN over the grouped rows, with the combine
@@ -80,6 +81,18 @@ typedef enum moe_expert_kind {
   MOE_EXPERT_SWIGLU = 1       /* expert(x) = (silu(x W1^T) * (x W3^T)) W2^T (iopenshare §5.2) */
 } moe_expert_kind;
 
+/* What happens to an assignment past its expert's capacity. */
+typedef enum moe_overflow {
+  MOE_OVERFLOW_DROP = 0,    /* dropped, adds nothing (tutorial Q2, Mixtral's choice;
+                               fde-learning "MoE 并行": overflow takes the residual path) */
+  MOE_OVERFLOW_REROUTE = 1, /* re-routed to the token's next-ranked expert with room,
+                               in rounds (fde-learning "MoE 并行", 推理时的负载均衡); see
+                               moe_reroute */
+  MOE_OVERFLOW_SHARED = 2   /* its weight goes to the shared expert, whose weight for the
+                               token becomes 1 + the sum of its dropped weights (tutorial
+                               Q2, DeepSeek-V3's choice; "MoE 并行" Q4); needs has_shared */
+} moe_overflow;
+
 /* The problem's parameters (fde-learning "MoE 并行" 关键参数: num_experts, top_k,
  * expert_capacity; tutorial §4.1 MoELayer(d_model, num_experts, top_k)). */
 typedef struct moe_shape {
@@ -93,6 +106,8 @@ typedef struct moe_shape {
   int32_t w_dtype;    /* moe_dtype of expert weights: BF16 or FP8_E4M3 (SWIGLU), F32 (LINEAR_BIAS) */
   int32_t kind;       /* moe_expert_kind */
   int32_t has_shared; /* 1: add one always-on SWIGLU shared expert (weight 1) */
+  int32_t overflow;   /* moe_overflow; 0 (drop) when zero-initialised */
+  int32_t reroute_rounds; /* MOE_OVERFLOW_REROUTE: re-routing rounds, 0..1024 */
 } moe_shape;
 
 /* Expert weights [device].  Unused members may be NULL. */
@@ -144,6 +159,31 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* W_g,
 moe_status moe_route_from_logits(const moe_shape* shape, const float* logits,
                                  int32_t* topk_idx, float* topk_w, void* stream);
 
+/* Overflow re-routing (fde-learning "MoE 并行", 推理时的负载均衡: when an expert
+ * is over capacity, its token goes to the next expert; iopenshare §4.2 leaves
+ * this step, redistribute, undefined).  Given the router's logits and top-k
+ * selection, final_idx[t, j] is the expert assignment (t, j) ends at, or -1:
+ *   - first pass: each expert keeps its first `capacity` assignments in token
+ *     order (the same keep mask as moe_dispatch);
+ *   - then `reroute_rounds` rounds (at most E - k do anything): every
+ *     assignment still without an expert, in token order then slot order,
+ *     asks for its token's next expert in logit order (equal logits: lower
+ *     index first) that the token has neither held nor asked for; each expert
+ *     admits the round's requests in that order while it has room;
+ *   - assignments still waiting after the last round get -1.
+ * A re-routed assignment keeps its routing weight topk_w[t, j].  With
+ * capacity == -1 nothing overflows and final_idx = topk_idx.  Pass final_idx
+ * to moe_dispatch (with the same shape) to group the rows; its -1 entries
+ * are skipped there.  shape->overflow is not consulted.
+ *   logits   [device] fp32 [T, E] (as moe_route writes them; the ranking is a pure
+ *            function of their bits)
+ *   topk_idx [device] int32 [T, k]; final_idx [device] int32 [T, k] output
+ *   ws       [device] workspace of moe_workspace_bytes(shape) bytes
+ * No host synchronisation. */
+moe_status moe_reroute(const moe_shape* shape, const float* logits,
+                       const int32_t* topk_idx, int32_t* final_idx, void* ws,
+                       void* stream);
+
 /* Load accounting and dispatch (tutorial §3.2 bincount; Q2 capacity and drop;
  * fde-learning Token Batching: group tokens by expert).
  *   counts[e]  [device] int32 [E]   assignments routed to e (before the drop)
@@ -156,8 +196,9 @@ moe_status moe_route_from_logits(const moe_shape* shape, const float* logits,
  *   x_perm     [device] [P_max, d] gathered rows x[perm_token[p]], or NULL
  * P_max = T*k without a capacity, min(T*k, E*capacity) with one.
  * The order is deterministic: within an expert, rows follow token order.
- * Expert ids outside [0, E) are ignored (counted nowhere, their slot_pos and
- * keep entries are left unwritten). */
+ * Expert ids outside [0, E) (such as moe_reroute's -1) stand for assignments
+ * without an expert: counted nowhere, slot_pos -1, keep 0.  Capacity is applied
+ * to the entries given, whatever shape->overflow says. */
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
                         const float* topk_w, const void* x, int32_t* counts,
                         int32_t* offsets, uint8_t* keep, int32_t* perm_token,
@@ -170,7 +211,8 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
  *   Exactly one of y_perm / y is non-NULL:
  *   y      [device] fp32 [T, d]: y[t] += perm_w[p] * expert_e(x[t]) for every grouped
  *          row (the combine fused into the last GEMM; y is NOT cleared here;
- *          the shared expert, if any, is added with weight 1 for every token)
+ *          the shared expert, if any, is added with weight 1 for every token;
+ *          MOE_OVERFLOW_SHARED is not available in this form: MOE_ERR_UNSUPPORTED)
  *   y_perm [device] fp32 [P_max (+ T with a shared expert), d]:
  *          y_perm[p] = expert_e(x[perm_token[p]]) (no weight) for p < P_max, and
  *          y_perm[P_max + t] = shared(x[t]) when there is a shared expert; finish
@@ -184,14 +226,19 @@ moe_status moe_expert_ffn(const moe_shape* shape, const moe_weights* w,
 /* Combine (MOE 学习笔记 输出聚合: weighted sum of the chosen experts' outputs):
  * y[t] = sum over kept j of topk_w[t, j] * y_perm[slot_pos[t, j]], in slot
  * order, then + y_perm[P_max + t] (weight 1) with a shared expert; dropped
- * assignments (slot_pos == -1) add nothing.  y_perm is laid out as
+ * assignments (slot_pos == -1) add nothing, except under MOE_OVERFLOW_SHARED,
+ * where the shared row's weight is 1 + the sum of the token's dropped topk_w.  y_perm is laid out as
  * moe_expert_ffn writes it; y [device] fp32 [T, d] is overwritten.  The sum
  * order is fixed, so the result is deterministic. */
 moe_status moe_combine(const moe_shape* shape, const float* y_perm,
                        const int32_t* slot_pos, const float* topk_w, float* y,
                        void* stream);
 
-/* The whole layer: route, dispatch, grouped FFN, combine, shared expert.
+/* The whole layer: route, dispatch, grouped FFN, combine, shared expert,
+ * with shape->overflow deciding what happens past capacity (re-routing as
+ * moe_reroute describes; overflow to the shared expert as moe_combine does).
+ * counts stays the router's loads before capacity; offsets are those of the
+ * final grouping.
  * With few rows per expert (P_max / E <= 32, decode-sized batches) the
  * combine is fused into the down projection as fp32 atomic adds into a
  * cleared y, so that projection can split K over workgroups; otherwise the

@@ -24,10 +24,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 DT_F32, DT_BF16, DT_FP8_E4M3 = 0, 1, 2
 LINEAR_BIAS, SWIGLU = 0, 1
+OVERFLOW_DROP, OVERFLOW_REROUTE, OVERFLOW_SHARED = 0, 1, 2
+OVERFLOW = {"drop": OVERFLOW_DROP, "reroute": OVERFLOW_REROUTE, "shared": OVERFLOW_SHARED}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_from_logits",
-           "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_reroute", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_load_imbalance", "moe_lpt_pack", "moe_timing_enable", "moe_timing_collect",
            "moe_timing_stage_name", "moe_last_error")
 
@@ -43,7 +45,8 @@ class Shape(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("kind", ctypes.c_int32),
-                ("has_shared", ctypes.c_int32)]
+                ("has_shared", ctypes.c_int32), ("overflow", ctypes.c_int32),
+                ("reroute_rounds", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -62,6 +65,8 @@ _lib.moe_route.restype = ctypes.c_int
 _lib.moe_route.argtypes = [_P(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_route_from_logits.restype = ctypes.c_int
 _lib.moe_route_from_logits.argtypes = [_P(Shape), _vp, _vp, _vp, _vp]
+_lib.moe_reroute.restype = ctypes.c_int
+_lib.moe_reroute.argtypes = [_P(Shape)] + [_vp] * 5
 _lib.moe_dispatch.restype = ctypes.c_int
 _lib.moe_dispatch.argtypes = [_P(Shape)] + [_vp] * 12
 _lib.moe_expert_ffn.restype = ctypes.c_int
@@ -109,9 +114,13 @@ def _check(st):
 
 
 def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=DT_BF16,
-               kind=SWIGLU, has_shared=False) -> Shape:
+               kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0) -> Shape:
+    """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared")."""
+    if isinstance(overflow, str):
+        overflow = OVERFLOW[overflow]
     return Shape(int(T), int(d), int(E), int(top_k), int(d_ff), int(capacity), int(act_dtype),
-                 int(w_dtype), int(kind), int(bool(has_shared)))
+                 int(w_dtype), int(kind), int(bool(has_shared)), int(overflow),
+                 int(reroute_rounds))
 
 
 def make_weights(**tensors) -> Weights:
@@ -181,6 +190,11 @@ def moe_route(shape, x, W_g, b_g, logits, topk_idx, topk_w, ws, stream=None):
 def moe_route_from_logits(shape, logits, topk_idx, topk_w, stream=None):
     _check(_lib.moe_route_from_logits(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx),
                                       _ptr(topk_w), _stream(stream)))
+
+
+def moe_reroute(shape, logits, topk_idx, final_idx, ws, stream=None):
+    _check(_lib.moe_reroute(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), _ptr(final_idx),
+                            _ptr(ws), _stream(stream)))
 
 
 def moe_dispatch(shape, topk_idx, topk_w, x, counts, offsets, keep, perm_token, perm_w,

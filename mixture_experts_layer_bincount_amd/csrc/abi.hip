@@ -46,6 +46,12 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
   if (s->top_k < 1 || s->top_k > s->E || s->top_k > 32)
     return fail(MOE_ERR_INVALID, "top_k=%d must be in [1, min(E, 32)]", s->top_k);
   if (s->capacity < -1) return fail(MOE_ERR_INVALID, "capacity=%d must be >= -1", s->capacity);
+  if (s->overflow < MOE_OVERFLOW_DROP || s->overflow > MOE_OVERFLOW_SHARED)
+    return fail(MOE_ERR_INVALID, "overflow=%d is not a moe_overflow", s->overflow);
+  if (s->reroute_rounds < 0 || s->reroute_rounds > 1024)
+    return fail(MOE_ERR_INVALID, "reroute_rounds=%d must be in [0, 1024]", s->reroute_rounds);
+  if (s->overflow == MOE_OVERFLOW_SHARED && !s->has_shared)
+    return fail(MOE_ERR_INVALID, "overflow to the shared expert needs has_shared");
   if (s->T * (int64_t)s->top_k > ((int64_t)1 << 31) - 1)
     return fail(MOE_ERR_INVALID, "T*top_k exceeds int32");
   if (s->kind == MOE_EXPERT_SWIGLU) {
@@ -119,6 +125,11 @@ moe_status check_weights(const moe_shape* s, const moe_weights* w) {
 }
 
 struct Ws {
+  RerouteWs rr;
+  int32_t* fin;
+  int32_t* cnt2;
+  float* logits;
+  float* shw;
   float* partial;
   void* wsplit;
   int32_t* chunk_hist;
@@ -130,9 +141,17 @@ struct Ws {
   float* Yp;
 };
 
+bool s_reroute(const WsLayout& L) { return L.off_logits != 0; }
+
 Ws carve(const WsLayout& L, void* ws) {
   char* b = (char*)ws;
-  return Ws{(float*)(b + L.off_partial),     (void*)(b + L.off_wsplit), (int32_t*)(b + L.off_chunk_hist),
+  return Ws{RerouteWs{(int32_t*)(b + L.off_cand), (int32_t*)(b + L.off_req),
+                      (int32_t*)(b + L.off_nxt), (int32_t*)(b + L.off_used),
+                      (int32_t*)(b + L.off_room)},
+            (int32_t*)(b + L.off_fin), (int32_t*)(b + L.off_cnt2),
+            s_reroute(L) ? (float*)(b + L.off_logits) : nullptr,
+            L.off_shw ? (float*)(b + L.off_shw) : nullptr,
+            (float*)(b + L.off_partial),     (void*)(b + L.off_wsplit), (int32_t*)(b + L.off_chunk_hist),
             (int32_t*)(b + L.off_chunk_base), (int32_t*)(b + L.off_perm_token),
             (float*)(b + L.off_perm_w),       (int32_t*)(b + L.off_slot_pos),
             (void*)(b + L.off_H),             L.grouped_combine ? (float*)(b + L.off_Yp) : nullptr};
@@ -217,6 +236,31 @@ WsLayout ws_layout(const moe_shape& s) {
   L.grouped_combine = use_grouped_combine(s);
   L.off_Yp = off;
   if (L.grouped_combine) off = align256(off + (size_t)L.H_rows * s.d * sizeof(float));
+  const int64_t KR = reroute_candidates(s);
+  L.off_cand = off;
+  off = align256(off + (size_t)std::max<int64_t>(s.T * KR, 1) * sizeof(int32_t));
+  L.off_fin = off;
+  off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
+  L.off_req = off;
+  off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
+  L.off_nxt = off;
+  off = align256(off + (size_t)std::max<int64_t>(s.T, 1) * sizeof(int32_t));
+  L.off_used = off;
+  off = align256(off + (size_t)s.E * sizeof(int32_t));
+  L.off_room = off;
+  off = align256(off + (size_t)s.E * sizeof(int32_t));
+  L.off_cnt2 = off;
+  off = align256(off + (size_t)s.E * sizeof(int32_t));
+  L.off_logits = 0;  // 0: not carved (offset 0 is the router partials)
+  if (s.overflow == MOE_OVERFLOW_REROUTE) {
+    L.off_logits = off;
+    off = align256(off + (size_t)std::max<int64_t>(s.T * s.E, 1) * sizeof(float));
+  }
+  L.off_shw = 0;
+  if (s.overflow == MOE_OVERFLOW_SHARED) {
+    L.off_shw = off;
+    off = align256(off + (size_t)std::max<int64_t>(s.T, 1) * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -286,6 +330,22 @@ moe_status moe_route_from_logits(const moe_shape* shape, const float* logits, in
                     "top-k");
 }
 
+moe_status moe_reroute(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
+                       int32_t* final_idx, void* ws, void* stream) {
+  MOE_TRY(check_shape(shape, false));
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk_idx, "topk_idx"));
+  MOE_TRY(check_ptr(final_idx, "final_idx"));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  const WsLayout L = ws_layout(s);
+  const Ws W = carve(L, ws);
+  return hip_status(launch_reroute(s, L, logits, topk_idx, final_idx, nullptr, W.rr,
+                                   W.chunk_hist, W.chunk_base, (hipStream_t)stream),
+                    "reroute");
+}
+
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const float* topk_w,
                         const void* x, int32_t* counts, int32_t* offsets, uint8_t* keep,
                         int32_t* perm_token, float* perm_w, int32_t* slot_pos, void* x_perm,
@@ -333,6 +393,9 @@ moe_status moe_expert_ffn(const moe_shape* shape, const moe_weights* w, const vo
   MOE_TRY(check_ptr(perm_token, "perm_token"));
   MOE_TRY(check_ptr(ws, "ws", 256));
   if (y) {
+    if (s.overflow == MOE_OVERFLOW_SHARED)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "overflow to the shared expert: use y_perm and moe_combine");
     MOE_TRY(check_ptr(y, "y", 16));
     MOE_TRY(check_ptr(perm_w, "perm_w"));
   } else {
@@ -387,12 +450,35 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   ce.begin(st);
   MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, W.wsplit, st), "router gemm"));
   ce.mark(1, st);
-  MOE_TRY(hip_status(launch_topk(s, W.partial, L.router_splits, b_g, nullptr, topk_idx, topk_w, st),
+  // re-routing needs the logits to rank each token's further candidates
+  const bool reroute = s.overflow == MOE_OVERFLOW_REROUTE && s.capacity >= 0 &&
+                       reroute_rounds_eff(s) > 0;
+  MOE_TRY(hip_status(launch_topk(s, W.partial, L.router_splits, b_g, reroute ? W.logits : nullptr,
+                                 topk_idx, topk_w, st),
                      "top-k"));
   ce.mark(2, st);
-  MOE_TRY(hip_status(launch_dispatch(s, L, topk_idx, topk_w, counts, offsets, nullptr, W.perm_token,
-                                     W.perm_w, W.slot_pos, W.chunk_hist, W.chunk_base, st),
-                     "dispatch"));
+  if (reroute) {
+    // final experts, then the grouping of those (capacity already respected)
+    MOE_TRY(hip_status(launch_reroute(s, L, W.logits, topk_idx, W.fin, counts, W.rr, W.chunk_hist,
+                                      W.chunk_base, st),
+                       "reroute"));
+    moe_shape s2 = s;
+    s2.capacity = -1;
+    MOE_TRY(hip_status(launch_dispatch(s2, L, W.fin, topk_w, W.cnt2, offsets, nullptr,
+                                       W.perm_token, W.perm_w, W.slot_pos, W.chunk_hist,
+                                       W.chunk_base, st),
+                       "dispatch"));
+  } else {
+    MOE_TRY(hip_status(launch_dispatch(s, L, topk_idx, topk_w, counts, offsets, nullptr,
+                                       W.perm_token, W.perm_w, W.slot_pos, W.chunk_hist,
+                                       W.chunk_base, st),
+                       "dispatch"));
+  }
+  const float* shared_w = nullptr;
+  if (s.overflow == MOE_OVERFLOW_SHARED && !L.grouped_combine) {
+    MOE_TRY(hip_status(launch_shared_weights(s, W.slot_pos, topk_w, W.shw, st), "shared weights"));
+    shared_w = W.shw;
+  }
   ce.mark(3, st);
   if (L.grouped_combine) {
     // grouped fp32 output, then the combine kernel writes every element of y
@@ -409,7 +495,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   MOE_TRY(hip_status(launch_fill_zero(y, s.T * (int64_t)s.d, st), "clear y"));
   ce.mark(4, st);
   const moe_status r = hip_status(launch_expert_ffn(s, L, *w, x, offsets, W.perm_token, W.perm_w,
-                                                    nullptr, y, W.H, st, ce.at(5)),
+                                                    nullptr, y, W.H, st, ce.at(5), shared_w),
                                   "expert ffn");
   ce.mark(6, st);
   ce.finish();

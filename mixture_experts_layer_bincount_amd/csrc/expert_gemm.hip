@@ -71,6 +71,7 @@ struct GemmParams {
   uint16_t* H;                // GATEUP output [H_rows, N]
   float* y;                   // DOWN output [T, N]
   float* y_perm;              // DOWN_PERM output [P_max, N]
+  const float* shared_w;      // MODE_DOWN: per-token weight of the shared expert (NULL: 1)
   int64_t A_bytes;            // size of the A operand buffer (< 2^31)
   int64_t T;
   int64_t P_max;
@@ -333,6 +334,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
           if (MODE == MODE_DOWN) {
             if (t.shared_e) {
               orow = m;
+              if (p.shared_w) wgt = p.shared_w[m];
             } else {
               orow = p.perm_token[t.seg + m];
               wgt = p.perm_w[t.seg + m];
@@ -798,15 +800,17 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
 }
 
 // Combine: y[t] = sum over kept j (in slot order) of topk_w[t, j] *
-// y_perm[slot_pos[t, j]], then + y_shared[t] (weight 1) when there is a
-// shared expert.  One thread per 4 consecutive outputs when d % 4 == 0.
+// y_perm[slot_pos[t, j]], then + sw * y_shared[t] when there is a shared
+// expert, with sw = 1, or with overflow to the shared expert 1 + the token's
+// dropped weights (summed in slot order).  One thread per 4 consecutive
+// outputs when d % 4 == 0.
 template <int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const float* __restrict__ y_shared,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const float* __restrict__ topk_w,
                                                       float* __restrict__ y, int64_t T, int k,
-                                                      int d) {
+                                                      int d, int shared_overflow) {
   const int dv = d / V;
   const int64_t n = T * dv;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
@@ -815,10 +819,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    float sw = 1.f;
     for (int j = 0; j < k; ++j) {
       const int32_t pos = slot_pos[t * k + j];
-      if (pos < 0) continue;
       const float w = topk_w[t * k + j];
+      if (pos < 0) {
+        sw += w;  // used only with overflow to the shared expert
+        continue;
+      }
       const float* src = y_perm + (int64_t)pos * d + c;
       if constexpr (V == 4) {
         const float4 v4 = *(const float4*)src;
@@ -829,8 +837,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     if (y_shared) {
       const float* src = y_shared + t * d + c;
+      if (!shared_overflow) sw = 1.f;
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += src[v];
+      for (int v = 0; v < V; ++v) acc[v] += sw * src[v];
     }
     if constexpr (V == 4)
       *(float4*)(y + t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -888,7 +897,7 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
 hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_weights& w,
                              const void* x, const int32_t* offsets, const int32_t* perm_token,
                              const float* perm_w, float* y_perm, float* y, void* H,
-                             hipStream_t st, hipEvent_t ev_mid) {
+                             hipStream_t st, hipEvent_t ev_mid, const float* shared_w) {
   if (s.kind == MOE_EXPERT_LINEAR_BIAS) {
     const int64_t n = L.P_max * s.d;
     const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
@@ -963,6 +972,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.H = nullptr;
   g2.y = y;
   g2.y_perm = y_perm;
+  g2.shared_w = shared_w;
   g2.K = s.d_ff;
   g2.N = s.d;
   const int bn2 = 256;  // output columns per down tile
@@ -986,13 +996,16 @@ hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm
                           const int32_t* slot_pos, const float* topk_w, float* y,
                           hipStream_t st) {
   const float* y_shared = s.has_shared ? y_perm + P_max * (int64_t)s.d : nullptr;
+  const int sh_ovf = (s.has_shared && s.overflow == MOE_OVERFLOW_SHARED) ? 1 : 0;
   const int V = (s.d % 4 == 0) ? 4 : 1;
   const int64_t n = s.T * (int64_t)(s.d / V);
   const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 16384));
   if (V == 4)
-    combine_kernel<4><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d);
+    combine_kernel<4><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d,
+                                              sh_ovf);
   else
-    combine_kernel<1><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d);
+    combine_kernel<1><<<blocks, 256, 0, st>>>(y_perm, y_shared, slot_pos, topk_w, y, s.T, s.top_k, s.d,
+                                              sh_ovf);
   return hipGetLastError();
 }
 

@@ -44,8 +44,33 @@ struct WsLayout {
   size_t off_slab;       // fp32  [tail_cap, 65536] split tail tiles (SwiGLU)
   bool grouped_combine;  // moe_forward: grouped output + combine instead of atomics
   size_t off_Yp;         // fp32  [H_rows, d] (grouped_combine only)
+  // overflow re-routing (always carved; small unless many rounds)
+  size_t off_cand;       // int32 [T, KR] experts by decreasing logit
+  size_t off_fin;        // int32 [T*k] expert each assignment holds
+  size_t off_req;        // int32 [T*k] the round's requests
+  size_t off_nxt;        // int32 [T] next candidate position per token
+  size_t off_used;       // int32 [E] fill per expert
+  size_t off_room;       // int32 [E] room per expert before the round
+  size_t off_cnt2;       // int32 [E] counts of the final grouping (not returned)
+  size_t off_logits;     // fp32  [T, E] (moe_forward with re-routing only)
+  size_t off_shw;        // fp32  [T] shared-expert weights (overflow to shared only)
   size_t total;
 };
+
+// Re-routing state carved from the workspace.
+struct RerouteWs {
+  int32_t* cand;
+  int32_t* req;
+  int32_t* nxt;
+  int32_t* used;
+  int32_t* room;
+};
+
+// Rounds that can change anything (each asks at least one new expert per
+// waiting slot): min(reroute_rounds, E - k); candidates per token needed:
+// KR = min(E, k * (1 + rounds)).
+int reroute_rounds_eff(const moe_shape& s);
+int reroute_candidates(const moe_shape& s);
 
 WsLayout ws_layout(const moe_shape& s);
 
@@ -69,6 +94,19 @@ hipError_t launch_dispatch(const moe_shape& s, const WsLayout& L,
                            int32_t* counts, int32_t* offsets, uint8_t* keep,
                            int32_t* perm_token, float* perm_w, int32_t* slot_pos,
                            int32_t* chunk_hist, int32_t* chunk_base, hipStream_t st);
+// Overflow re-routing: fin[T*k] receives each assignment's final expert or
+// -1; counts (if given) the router's loads per expert.
+hipError_t launch_reroute(const moe_shape& s, const WsLayout& L, const float* logits,
+                          const int32_t* topk_idx, int32_t* fin, int32_t* counts,
+                          const RerouteWs& R, int32_t* chunk_hist, int32_t* chunk_base,
+                          hipStream_t st);
+// Ranked candidates cand[t, 0..KR) of every token: experts by decreasing
+// logit, equal logits lower index first (the top-k order continued).
+hipError_t launch_candidates(const moe_shape& s, const float* logits, int KR, int32_t* cand,
+                             hipStream_t st);
+// shared_w[t] = 1 + sum of the token's dropped topk_w (slot_pos == -1).
+hipError_t launch_shared_weights(const moe_shape& s, const int32_t* slot_pos,
+                                 const float* topk_w, float* shared_w, hipStream_t st);
 hipError_t launch_gather(const moe_shape& s, int64_t P_max, const int32_t* offsets,
                          const int32_t* perm_token, const void* x, void* x_perm,
                          hipStream_t st);
@@ -79,7 +117,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L,
                              const moe_weights& w, const void* x,
                              const int32_t* offsets, const int32_t* perm_token,
                              const float* perm_w, float* y_perm, float* y,
-                             void* H, hipStream_t st, hipEvent_t ev_mid = nullptr);
+                             void* H, hipStream_t st, hipEvent_t ev_mid = nullptr,
+                             const float* shared_w = nullptr);
 
 // y_perm holds P_max grouped rows, then (with a shared expert) T rows of
 // the shared expert's output.

@@ -264,6 +264,38 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
 }
 
+// Ranked candidates for overflow re-routing: the top-k selection continued
+// to KR experts, with the same key (logit bits, then the lower index), so
+// cand[t, 0..k) equals the top-k choice.  L lanes per token.
+template <int L, int EPL>
+__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ logits,
+                                                         int64_t T, int E, int KR,
+                                                         int32_t* __restrict__ cand) {
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = gt / L;
+  const int sub = (int)(gt % L);
+  const bool live = t < T;
+  uint64_t keys[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = sub + i * L;
+    keys[i] = (live && e < E) ? topk_key(logits[t * E + e], e) : 0;
+  }
+  for (int j = 0; j < KR; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) best = keys[i] > best ? keys[i] : best;
+    best = group_max_u64<L>(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    if (live && sub == 0) cand[t * KR + j] = e;
+    if ((e % L) == sub) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (i == e / L) keys[i] = 0;
+    }
+  }
+}
+
 template <typename XT>
 hipError_t router_gemm_dispatch(const moe_shape& s, const XT* x, const float* W_g,
                                 float* partial, int splits, hipStream_t st) {
@@ -363,6 +395,30 @@ hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
   if (s.E <= 512) MOE_TK(64, 8)
   if (s.E <= 1024) MOE_TK(64, 16)
 #undef MOE_TK
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_candidates(const moe_shape& s, const float* logits, int KR, int32_t* cand,
+                             hipStream_t st) {
+#define MOE_CK(LL, EPL)                                                                    \
+  {                                                                                        \
+    const int64_t n = s.T * LL;                                                            \
+    candidates_kernel<LL, EPL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(logits, s.T,   \
+                                                                            s.E, KR, cand); \
+    return hipGetLastError();                                                              \
+  }
+  if (s.E <= 1) MOE_CK(1, 1)
+  if (s.E <= 2) MOE_CK(2, 1)
+  if (s.E <= 4) MOE_CK(4, 1)
+  if (s.E <= 8) MOE_CK(8, 1)
+  if (s.E <= 16) MOE_CK(16, 1)
+  if (s.E <= 32) MOE_CK(32, 1)
+  if (s.E <= 64) MOE_CK(64, 1)
+  if (s.E <= 128) MOE_CK(64, 2)
+  if (s.E <= 256) MOE_CK(64, 4)
+  if (s.E <= 512) MOE_CK(64, 8)
+  if (s.E <= 1024) MOE_CK(64, 16)
+#undef MOE_CK
   return hipErrorInvalidValue;
 }
 

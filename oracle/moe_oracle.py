@@ -333,15 +333,16 @@ def _shared_weight(w, final, overflow):
 
 
 def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
-                   shared=None, idx_override=None, overflow="drop", rounds=0):
+                   shared=None, idx_override=None, overflow="drop", rounds=0, logits=None):
     """The same layer evaluated only at the given tokens.
 
     Routing, counts and capacity ranks are computed for all T tokens (a
     token's drop depends on every earlier token), the expert evaluation only
     for the requested rows.  Experts are visited one at a time so each
     expert's weights are widened once.  Returns (y_rows [len(tokens), d],
-    full routing/dispatch dict)."""
-    logits = router_logits(x, W_g, b_g)
+    full routing/dispatch dict).  logits: as in forward()."""
+    if logits is None:
+        logits = router_logits(x, W_g, b_g)
     if idx_override is None:
         idx, w = route(logits, k)
     else:

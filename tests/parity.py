@@ -11,6 +11,7 @@ from moe_synth import Workload
 
 MARGIN_EXCLUDE = 1e-5            # tokens with a smaller top-k margin may flip
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_e4m3": 6e-2}
+LOGIT_TOL = 1e-4                 # fp32 router logits against the float64 oracle
 
 
 def tolerance(cfg) -> float:
@@ -21,7 +22,7 @@ def oracle_capacity(cfg) -> int:
     return oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.cf)
 
 
-def gpu_forward(wl: Workload, dev=None):
+def gpu_forward(wl: Workload, dev=None, overflow="drop", rounds=0):
     """Run moe_forward once on the workload; returns (numpy outputs, layer, dev)."""
     import torch
 
@@ -33,13 +34,29 @@ def gpu_forward(wl: Workload, dev=None):
     cap = moe.moe_capacity(c.T, c.E, c.k, c.cf) if c.cf else -1
     layer = moe.MoELayer(c.T, c.d, c.E, c.k, c.d_ff, W_g=dev["W_g"], b_g=dev["b_g"],
                          weights=dev["weights"], capacity=cap, kind=c.kind, w_dtype=c.w,
-                         has_shared=c.shared)
+                         has_shared=c.shared, overflow=overflow, reroute_rounds=rounds)
     layer(dev["x"])
     torch.cuda.synchronize()
     out = dict(y=layer.y.cpu().numpy(), idx=layer.topk_idx.cpu().numpy(),
                w=layer.topk_w.cpu().numpy(), counts=layer.counts.cpu().numpy(),
                offsets=layer.offsets.cpu().numpy())
     return out, layer, dev
+
+
+def gpu_logits(layer, dev) -> np.ndarray:
+    """The router logits moe_forward decides on: moe_route on the same shape
+    runs the same router kernels in the same configuration, so its fp32
+    logits are those moe_forward's selection (and re-routing) used."""
+    import torch
+
+    import mixture_experts_layer_bincount_amd as moe
+    s = layer.shape
+    logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((s.T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.top_k), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, dev["x"], dev["W_g"], dev["b_g"], logits, idx, w, moe.workspace(s))
+    torch.cuda.synchronize()
+    return logits.cpu().numpy()
 
 
 def check_routing(logits, k, gpu_idx, gpu_w, w_tol=1e-5):
@@ -63,27 +80,45 @@ def rel_err(y, y_ref) -> float:
     return float(np.abs(y - y_ref).max() / max(rms, 1e-30))
 
 
-def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None) -> dict:
+def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None, overflow="drop", rounds=0,
+                  decide_on=None) -> dict:
     """Compare one moe_forward result with the oracle (on all tokens, or on
-    the sampled `tokens`).  Returns a report dict."""
+    the sampled `tokens`).  Returns a report dict.
+
+    decide_on: the GPU's fp32 logits (gpu_logits()).  When given, the
+    oracle's routing decisions (top-k, and the ranking that re-routing
+    follows past the top-k) are taken on those same fp32 values, after the
+    logits themselves are checked against the oracle's float64 logits."""
     c = wl.cfg
     C = oracle_capacity(c)
     x = wl.x()
     W_g = wl.W_g()
     b_g = wl.b_g()
     logits = oracle.router_logits(x, W_g, b_g)
-    flip = check_routing(logits, c.k, gpu["idx"], gpu["w"])
-    override = gpu["idx"] if flip.any() else None
+    if decide_on is None:
+        flip = check_routing(logits, c.k, gpu["idx"], gpu["w"])
+        override = gpu["idx"] if flip.any() else None
+    else:
+        lerr = rel_err(decide_on.astype(np.float64), logits)
+        assert lerr <= LOGIT_TOL, f"router logits: max-abs-err/RMS = {lerr:.3e}"
+        o_idx, o_w = oracle.route(decide_on, c.k)
+        assert np.array_equal(gpu["idx"], o_idx), "top-k differs on the same fp32 logits"
+        assert np.abs(gpu["w"] - o_w).max() <= 1e-5, "routing weights differ"
+        logits = decide_on.astype(np.float64)
+        flip = np.zeros(c.T, dtype=bool)
+        override = None
     shared = wl.shared if c.shared else None
+    pol = dict(overflow=overflow, rounds=rounds)
     if tokens is None:
         r = oracle.forward(x, W_g, b_g, c.k, c.E, wl.expert, kind=c.kind, C=C,
-                           shared=shared, idx_override=override, logits=logits)
+                           shared=shared, idx_override=override, logits=logits, **pol)
         y_ref = r["y"]
         y = gpu["y"]
     else:
         tokens = np.asarray(tokens)
         y_ref, r = oracle.forward_tokens(tokens, x, W_g, b_g, c.k, c.E, wl.expert, kind=c.kind,
-                                         C=C, shared=shared, idx_override=override)
+                                         C=C, shared=shared, idx_override=override,
+                                         logits=logits, **pol)
         y = gpu["y"][tokens]
     # load accounting is bit-exact given the same selection
     assert np.array_equal(gpu["counts"], r["counts"]), "counts differ"
@@ -92,4 +127,4 @@ def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None) -> dict:
     tol = tolerance(c) if tol is None else tol
     assert err <= tol, f"max-abs-err/RMS = {err:.3e} > {tol}"
     return dict(err=err, flipped=int(flip.sum()), tol=tol, kept=int(r["offsets"][-1]),
-                counts=r["counts"])
+                counts=r["counts"], C=C)

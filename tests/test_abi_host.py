@@ -79,10 +79,12 @@ def test_workspace_bytes_degenerate(moe, T, d, E, k):
     (dict(T=-1), "T="), (dict(E=0), "E="), (dict(top_k=9), "top_k"), (dict(top_k=0), "top_k"),
     (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 64"),
     (dict(d_ff=100), "d_ff"), (dict(act_dtype=0), "bf16 x"), (dict(w_dtype=0), "weights"),
-    (dict(kind=7), "kind")])
+    (dict(kind=7), "kind"), (dict(overflow=3), "overflow="),
+    (dict(reroute_rounds=-1), "reroute_rounds"), (dict(reroute_rounds=1025), "reroute_rounds"),
+    (dict(overflow=2), "has_shared")])
 def test_validation_rejects_bad_shapes(moe, kw, needle):
     base = dict(T=16, d=256, E=8, top_k=2, d_ff=128, capacity=-1, act_dtype=1, w_dtype=1,
-                kind=1, has_shared=False)
+                kind=1, has_shared=False, overflow=0, reroute_rounds=0)
     base.update(kw)
     s = moe.make_shape(**base)
     fake = 256  # never dereferenced: validation fails first
@@ -110,3 +112,16 @@ def test_validation_null_and_alignment(moe):
     with pytest.raises(moe.MoEError, match="shared"):
         moe.moe_forward(moe.make_shape(16, 8, 4, 2, 0, -1, 0, 0, 0, True), 256, 256, None,
                         moe.make_weights(W=256, b=256), 256, 256, 256, 256, 256, 256, stream=0)
+
+
+def test_workspace_covers_rerouting(moe):
+    """The re-routing state grows with the rounds (candidates per token) and
+    the logits buffer appears only for moe_forward's re-routing policy."""
+    base = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160))
+    r1 = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160,
+                                                overflow="reroute", reroute_rounds=1))
+    r8 = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160,
+                                                overflow="reroute", reroute_rounds=8))
+    assert r1 >= base + 4096 * 64 * 4          # fp32 logits
+    assert r8 >= r1 + 4096 * 2 * 7 * 4         # 14 more candidates per token
+

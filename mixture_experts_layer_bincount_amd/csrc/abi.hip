@@ -128,7 +128,6 @@ struct Ws {
   RerouteWs rr;
   int32_t* fin;
   int32_t* cnt2;
-  float* logits;
   float* shw;
   float* partial;
   void* wsplit;
@@ -141,15 +140,12 @@ struct Ws {
   float* Yp;
 };
 
-bool s_reroute(const WsLayout& L) { return L.off_logits != 0; }
-
 Ws carve(const WsLayout& L, void* ws) {
   char* b = (char*)ws;
   return Ws{RerouteWs{(int32_t*)(b + L.off_cand), (int32_t*)(b + L.off_req),
                       (int32_t*)(b + L.off_nxt), (int32_t*)(b + L.off_used),
                       (int32_t*)(b + L.off_room)},
             (int32_t*)(b + L.off_fin), (int32_t*)(b + L.off_cnt2),
-            s_reroute(L) ? (float*)(b + L.off_logits) : nullptr,
             L.off_shw ? (float*)(b + L.off_shw) : nullptr,
             (float*)(b + L.off_partial),     (void*)(b + L.off_wsplit), (int32_t*)(b + L.off_chunk_hist),
             (int32_t*)(b + L.off_chunk_base), (int32_t*)(b + L.off_perm_token),
@@ -200,7 +196,8 @@ WsLayout ws_layout(const moe_shape& s) {
   WsLayout L{};
   const int64_t A = s.T * (int64_t)s.top_k;
   L.router_splits = router_splits_for(s);
-  L.nchunks = (int)std::max<int64_t>(1, (A + kDispatchChunk - 1) / kDispatchChunk);
+  const int chunk = dispatch_chunk(s.top_k);
+  L.nchunks = (int)std::max<int64_t>(1, (A + chunk - 1) / chunk);
   L.P_max = (s.capacity < 0) ? A : std::min<int64_t>(A, (int64_t)s.E * s.capacity);
   L.H_rows = L.P_max + (s.has_shared ? s.T : 0);
   size_t off = 0;
@@ -251,12 +248,7 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align256(off + (size_t)s.E * sizeof(int32_t));
   L.off_cnt2 = off;
   off = align256(off + (size_t)s.E * sizeof(int32_t));
-  L.off_logits = 0;  // 0: not carved (offset 0 is the router partials)
-  if (s.overflow == MOE_OVERFLOW_REROUTE) {
-    L.off_logits = off;
-    off = align256(off + (size_t)std::max<int64_t>(s.T * s.E, 1) * sizeof(float));
-  }
-  L.off_shw = 0;
+  L.off_shw = 0;  // 0: not carved (offset 0 is the router partials)
   if (s.overflow == MOE_OVERFLOW_SHARED) {
     L.off_shw = off;
     off = align256(off + (size_t)std::max<int64_t>(s.T, 1) * sizeof(float));
@@ -341,8 +333,14 @@ moe_status moe_reroute(const moe_shape* shape, const float* logits, const int32_
   MOE_TRY(check_ptr(ws, "ws", 256));
   const WsLayout L = ws_layout(s);
   const Ws W = carve(L, ws);
-  return hip_status(launch_reroute(s, L, logits, topk_idx, final_idx, nullptr, W.rr,
-                                   W.chunk_hist, W.chunk_base, (hipStream_t)stream),
+  hipStream_t st = (hipStream_t)stream;
+  // the ranking past the top-k: the top-k selection continued on the same logits
+  if (reroute_rounds_eff(s) > 0 && s.capacity >= 0)
+    MOE_TRY(hip_status(launch_topk(s, logits, 1, nullptr, nullptr, nullptr, nullptr, st,
+                                   W.rr.cand, reroute_candidates(s)),
+                       "candidates"));
+  return hip_status(launch_reroute(s, L, topk_idx, final_idx, nullptr, W.rr, W.chunk_hist,
+                                   W.chunk_base, st),
                     "reroute");
 }
 
@@ -450,23 +448,24 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   ce.begin(st);
   MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, W.wsplit, st), "router gemm"));
   ce.mark(1, st);
-  // re-routing needs the logits to rank each token's further candidates
+  // re-routing: the top-k kernel also lists each token's further candidates
   const bool reroute = s.overflow == MOE_OVERFLOW_REROUTE && s.capacity >= 0 &&
                        reroute_rounds_eff(s) > 0;
-  MOE_TRY(hip_status(launch_topk(s, W.partial, L.router_splits, b_g, reroute ? W.logits : nullptr,
-                                 topk_idx, topk_w, st),
+  MOE_TRY(hip_status(launch_topk(s, W.partial, L.router_splits, b_g, nullptr, topk_idx, topk_w,
+                                 st, reroute ? W.rr.cand : nullptr,
+                                 reroute ? reroute_candidates(s) : 0),
                      "top-k"));
   ce.mark(2, st);
   if (reroute) {
     // final experts, then the grouping of those (capacity already respected)
-    MOE_TRY(hip_status(launch_reroute(s, L, W.logits, topk_idx, W.fin, counts, W.rr, W.chunk_hist,
+    MOE_TRY(hip_status(launch_reroute(s, L, topk_idx, W.fin, counts, W.rr, W.chunk_hist,
                                       W.chunk_base, st),
                        "reroute"));
     moe_shape s2 = s;
     s2.capacity = -1;
     MOE_TRY(hip_status(launch_dispatch(s2, L, W.fin, topk_w, W.cnt2, offsets, nullptr,
                                        W.perm_token, W.perm_w, W.slot_pos, W.chunk_hist,
-                                       W.chunk_base, st),
+                                       W.chunk_base, st, /*hist_ready=*/true),
                        "dispatch"));
   } else {
     MOE_TRY(hip_status(launch_dispatch(s, L, topk_idx, topk_w, counts, offsets, nullptr,

@@ -29,7 +29,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
   int router_splits;     // split-K factor of the router GEMM
-  int nchunks;           // dispatch chunks of kDispatchChunk assignments
+  int nchunks;           // dispatch chunks of dispatch_chunk(k) assignments
   int64_t P_max;         // upper bound of kept assignments
   int64_t H_rows;        // rows of the hidden buffer (P_max + T for a shared expert)
   size_t off_partial;    // fp32 [router_splits, T, E]
@@ -52,7 +52,6 @@ struct WsLayout {
   size_t off_used;       // int32 [E] fill per expert
   size_t off_room;       // int32 [E] room per expert before the round
   size_t off_cnt2;       // int32 [E] counts of the final grouping (not returned)
-  size_t off_logits;     // fp32  [T, E] (moe_forward with re-routing only)
   size_t off_shw;        // fp32  [T] shared-expert weights (overflow to shared only)
   size_t total;
 };
@@ -85,25 +84,30 @@ int router_splits_for(const moe_shape& s);
 size_t router_split_bytes(const moe_shape& s);
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
                               float* partial, int splits, void* split_ws, hipStream_t st);
+// cand (optional): the selection continued to KR experts per token, cand[t,
+// 0..KR) by decreasing logit (the ranking overflow re-routing follows).
+// topk_idx / topk_w may be NULL when only cand is wanted.
 hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
                        const float* b_g, float* logits, int32_t* topk_idx,
-                       float* topk_w, hipStream_t st);
+                       float* topk_w, hipStream_t st, int32_t* cand = nullptr, int KR = 0);
 
 hipError_t launch_dispatch(const moe_shape& s, const WsLayout& L,
                            const int32_t* topk_idx, const float* topk_w,
                            int32_t* counts, int32_t* offsets, uint8_t* keep,
                            int32_t* perm_token, float* perm_w, int32_t* slot_pos,
-                           int32_t* chunk_hist, int32_t* chunk_base, hipStream_t st);
+                           int32_t* chunk_hist, int32_t* chunk_base, hipStream_t st,
+                           bool hist_ready = false);
+// Assignments per dispatch chunk: a multiple of k, so a token's slots share
+// one chunk.
+int dispatch_chunk(int k);
 // Overflow re-routing: fin[T*k] receives each assignment's final expert or
-// -1; counts (if given) the router's loads per expert.
-hipError_t launch_reroute(const moe_shape& s, const WsLayout& L, const float* logits,
-                          const int32_t* topk_idx, int32_t* fin, int32_t* counts,
-                          const RerouteWs& R, int32_t* chunk_hist, int32_t* chunk_base,
-                          hipStream_t st);
-// Ranked candidates cand[t, 0..KR) of every token: experts by decreasing
-// logit, equal logits lower index first (the top-k order continued).
-hipError_t launch_candidates(const moe_shape& s, const float* logits, int KR, int32_t* cand,
-                             hipStream_t st);
+// -1; counts (if given) the router's loads per expert.  R.cand must hold the
+// ranked candidates (launch_topk with KR = reroute_candidates(s)).  On
+// return chunk_hist holds the per-chunk histogram of fin, ready for
+// launch_dispatch(..., hist_ready = true) over fin.
+hipError_t launch_reroute(const moe_shape& s, const WsLayout& L, const int32_t* topk_idx,
+                          int32_t* fin, int32_t* counts, const RerouteWs& R,
+                          int32_t* chunk_hist, int32_t* chunk_base, hipStream_t st);
 // shared_w[t] = 1 + sum of the token's dropped topk_w (slot_pos == -1).
 hipError_t launch_shared_weights(const moe_shape& s, const int32_t* slot_pos,
                                  const float* topk_w, float* shared_w, hipStream_t st);

@@ -221,7 +221,7 @@ template <int L, int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ partial, int splits, const float* __restrict__ b_g,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int64_t T, int E, int k) {
+    float* __restrict__ topk_w, int64_t T, int E, int k, int32_t* __restrict__ cand, int KR) {
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = gt / L;
   const int sub = (int)(gt % L);
@@ -241,7 +241,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
   int my_e = -1;
   float my_v = 0.f, vmax = 0.f;
-  for (int j = 0; j < k; ++j) {
+  const int rounds = cand ? max(k, KR) : k;
+  for (int j = 0; j < rounds; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) best = keys[i] > best ? keys[i] : best;
@@ -249,7 +250,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
     const float v = key_value(best);
     if (j == 0) vmax = v;
-    if (sub == j) { my_e = e; my_v = v; }
+    if (sub == j && j < k) { my_e = e; my_v = v; }
+    if (cand && live && sub == 0 && j < KR) cand[t * KR + j] = e;
     if ((e % L) == sub) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
@@ -258,41 +260,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
   const float ex = (sub < k) ? expf(my_v - vmax) : 0.f;
   const float den = group_sum<L>(ex);
-  if (live && sub < k) {
+  if (live && sub < k && topk_idx) {
     topk_idx[t * k + sub] = my_e;
     topk_w[t * k + sub] = ex / den;
-  }
-}
-
-// Ranked candidates for overflow re-routing: the top-k selection continued
-// to KR experts, with the same key (logit bits, then the lower index), so
-// cand[t, 0..k) equals the top-k choice.  L lanes per token.
-template <int L, int EPL>
-__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ logits,
-                                                         int64_t T, int E, int KR,
-                                                         int32_t* __restrict__ cand) {
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = gt / L;
-  const int sub = (int)(gt % L);
-  const bool live = t < T;
-  uint64_t keys[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = sub + i * L;
-    keys[i] = (live && e < E) ? topk_key(logits[t * E + e], e) : 0;
-  }
-  for (int j = 0; j < KR; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) best = keys[i] > best ? keys[i] : best;
-    best = group_max_u64<L>(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if (live && sub == 0) cand[t * KR + j] = e;
-    if ((e % L) == sub) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (i == e / L) keys[i] = 0;
-    }
   }
 }
 
@@ -374,13 +344,13 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_
 
 hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
                        const float* b_g, float* logits, int32_t* topk_idx,
-                       float* topk_w, hipStream_t st) {
+                       float* topk_w, hipStream_t st, int32_t* cand, int KR) {
   const int64_t threads_needed = s.T;  // multiplied by L below
 #define MOE_TK(LL, EPL)                                                                    \
   {                                                                                        \
     const int64_t n = threads_needed * LL;                                                 \
     topk_kernel<LL, EPL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(                     \
-        partial, splits, b_g, logits, topk_idx, topk_w, s.T, s.E, s.top_k);                \
+        partial, splits, b_g, logits, topk_idx, topk_w, s.T, s.E, s.top_k, cand, KR);      \
     return hipGetLastError();                                                              \
   }
   if (s.E <= 1) MOE_TK(1, 1)
@@ -395,30 +365,6 @@ hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
   if (s.E <= 512) MOE_TK(64, 8)
   if (s.E <= 1024) MOE_TK(64, 16)
 #undef MOE_TK
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_candidates(const moe_shape& s, const float* logits, int KR, int32_t* cand,
-                             hipStream_t st) {
-#define MOE_CK(LL, EPL)                                                                    \
-  {                                                                                        \
-    const int64_t n = s.T * LL;                                                            \
-    candidates_kernel<LL, EPL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(logits, s.T,   \
-                                                                            s.E, KR, cand); \
-    return hipGetLastError();                                                              \
-  }
-  if (s.E <= 1) MOE_CK(1, 1)
-  if (s.E <= 2) MOE_CK(2, 1)
-  if (s.E <= 4) MOE_CK(4, 1)
-  if (s.E <= 8) MOE_CK(8, 1)
-  if (s.E <= 16) MOE_CK(16, 1)
-  if (s.E <= 32) MOE_CK(32, 1)
-  if (s.E <= 64) MOE_CK(64, 1)
-  if (s.E <= 128) MOE_CK(64, 2)
-  if (s.E <= 256) MOE_CK(64, 4)
-  if (s.E <= 512) MOE_CK(64, 8)
-  if (s.E <= 1024) MOE_CK(64, 16)
-#undef MOE_CK
   return hipErrorInvalidValue;
 }
 

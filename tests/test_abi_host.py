@@ -115,13 +115,16 @@ def test_validation_null_and_alignment(moe):
 
 
 def test_workspace_covers_rerouting(moe):
-    """The re-routing state grows with the rounds (candidates per token) and
-    the logits buffer appears only for moe_forward's re-routing policy."""
+    """The re-routing state grows with the rounds: k more ranked candidates
+    per token and round, up to E."""
     base = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160))
     r1 = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160,
                                                 overflow="reroute", reroute_rounds=1))
     r8 = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160,
                                                 overflow="reroute", reroute_rounds=8))
-    assert r1 >= base + 4096 * 64 * 4          # fp32 logits
-    assert r8 >= r1 + 4096 * 2 * 7 * 4         # 14 more candidates per token
+    assert r1 >= base + 4096 * 2 * 4           # 2 more candidates per token
+    assert r8 >= r1 + 4096 * 2 * 7 * 4         # 14 more
+    r99 = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, capacity=160,
+                                                 overflow="reroute", reroute_rounds=99))
+    assert r99 - base < 4096 * 64 * 4 + 4096   # capped at E candidates
 

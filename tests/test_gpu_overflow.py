@@ -73,6 +73,8 @@ def _skewed_logits(T, E, seed, ties):
     (500, 256, 8, 12, 2, True),       # 256 experts, k = 8
     (129, 1024, 32, 3, 2, False),     # 1024 experts, k = 32 (KR = 96)
     (700, 6, 3, 300, 4, True),        # more rounds than E - k: capped at 3
+    (1500, 24, 5, 220, 3, True),      # k = 5: chunks of 1020 assignments
+    (2000, 12, 6, 800, 2, False),     # k = 6: chunks of 1020 assignments
     (400, 8, 2, 0, 3, False),         # C = 0: nothing placed
     (400, 8, 2, 100, 0, False),       # zero rounds: the capacity drop
     (300, 8, 2, -1, 2, True),         # unlimited capacity: unchanged

@@ -100,7 +100,9 @@ def _skewed_selection(T, E, k, seed, skew):
 @pytest.mark.parametrize("T,E,k,C,skew", [
     (64, 4, 2, -1, 0.0), (64, 4, 2, 20, 0.0), (5000, 8, 2, -1, 0.0), (5000, 8, 2, 900, 1.0),
     (3000, 64, 2, 100, 1.5), (16384, 64, 2, 640, 1.5), (4096, 256, 8, -1, 0.0),
-    (700, 256, 8, 10, 2.0), (1, 8, 2, -1, 0.0), (513, 16, 4, 0, 0.0), (999, 1024, 32, 40, 0.5)])
+    (700, 256, 8, 10, 2.0), (1, 8, 2, -1, 0.0), (513, 16, 4, 0, 0.0), (999, 1024, 32, 40, 0.5),
+    # k not a power of two: chunks of 1023 / 1020 assignments, whole tokens each
+    (2000, 16, 3, 300, 1.0), (1500, 32, 6, 200, 1.5), (777, 12, 5, -1, 0.0)])
 def test_dispatch_bit_exact(moe, T, E, k, C, skew):
     print(f"[dispatch] T={T} E={E} k={k} C={C}", flush=True)
     o_idx, o_w = _skewed_selection(T, E, k, seed=T + E, skew=skew)

@@ -13,6 +13,9 @@ per expert.
 Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
   router_logits        pinned (one-hot closed form, shift invariance)
   route                pinned (tutorial Q1 worked example, k=1, k=E, identities)
+  select_groups / grouped route   pinned (hand-worked example in tests/golden,
+                       all groups = plain routing, one expert per group = plain
+                       routing, pairwise group-order brute force)
   bincount             pinned (sum = T*k, tutorial §3.2 total, brute force)
   capacity             pinned (definition bounds, tutorial Q2 example, skew workload value)
   capacity_ranks / dispatch   pinned (tutorial Q2 example, brute-force invariants)
@@ -30,7 +33,7 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
                        print no outputs for those shapes)
 """
 from .moe_oracle import (  # noqa: F401
-    widen, router_logits, select_topk, route, route_softmax_of_topk,
+    widen, router_logits, select_topk, select_groups, route, route_softmax_of_topk,
     bincount, capacity, capacity_ranks, dispatch, reroute, silu, expert_linear_bias,
     expert_swiglu, forward, forward_tokens, dense_forward, topk_margin,
 )

@@ -6,7 +6,11 @@ give it:
   router      logits = x . W_g (+ b)            iopenshare "MoE 混合专家架构" §2.1
                                                 (TopKGating: gate Linear, no bias);
                                                 adv12 tutorial §3.1 / §4.1
-  top-k       keep the k experts with the largest logits (ties: lower index)
+  top-k       keep the k experts with the largest logits (ties: lower index);
+              optionally only among the experts of the token's best groups
+              (group-limited routing)          fde-learning "MoE 并行"
+                                                (Hierarchical Routing); tutorial
+                                                §5 (device-limited routing)
   weights     softmax over all experts, keep the k selected probabilities and
               divide by their sum                tutorial §4.1 table steps 1-3, Q1
   bincount    load[e] = number of (token, slot) pairs routed to e    tutorial §3.2
@@ -96,9 +100,37 @@ def weights_for(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(logits: np.ndarray, k: int):
-    """(topk_idx [T,k] int32, topk_w [T,k] float64)."""
-    idx = select_topk(logits, k)
+def select_groups(logits: np.ndarray, groups: int, topk_groups: int) -> np.ndarray:
+    """Group-limited routing, step 1: which expert groups each token may use.
+
+    fde-learning "MoE 并行" (通信瓶颈的缓解策略, Hierarchical Routing: choose
+    a group first, then an expert) and the tutorial's DeepSeek-V3 notes
+    (device-limited routing: a token's experts lie on at most M devices).
+    The E experts form `groups` equal groups of consecutive indices; a
+    group's score for a token is its largest logit; the token keeps the
+    `topk_groups` groups with the largest scores (equal scores: the lower
+    group first).  Returns a bool mask [T, groups]."""
+    l64 = np.asarray(logits, dtype=np.float64) + 0.0
+    T, E = l64.shape
+    score = l64.reshape(T, groups, E // groups).max(axis=2)
+    g_idx = np.broadcast_to(np.arange(groups), (T, groups))
+    order = np.lexsort((g_idx, -score), axis=-1)[:, :topk_groups]
+    mask = np.zeros((T, groups), dtype=bool)
+    np.put_along_axis(mask, order, True, axis=1)
+    return mask
+
+
+def route(logits: np.ndarray, k: int, groups: int = 0, topk_groups: int = 0):
+    """(topk_idx [T,k] int32, topk_w [T,k] float64).  With groups > 1 the
+    top-k is taken among the experts of the kept groups only
+    (select_groups); the weights follow the same rule as without groups."""
+    if groups > 1:
+        T, E = logits.shape
+        allowed = np.repeat(select_groups(logits, groups, topk_groups), E // groups, axis=1)
+        masked = np.where(allowed, np.asarray(logits, dtype=np.float64), -np.inf)
+        idx = select_topk(masked, k)
+    else:
+        idx = select_topk(logits, k)
     return idx, weights_for(logits, idx)
 
 
@@ -265,7 +297,8 @@ def _expert_fn(kind: str):
 
 # ---------------------------------------------------------------- layer
 def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
-            idx_override=None, logits=None, overflow="drop", rounds=0):
+            idx_override=None, logits=None, overflow="drop", rounds=0, groups=0,
+            topk_groups=0):
     """The whole layer, masked loop over experts (tutorial §3.1).
 
     expert(e) -> dict of that expert's weights; shared() -> dict or None.
@@ -276,7 +309,8 @@ def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
     overflow: "drop" (dropped assignments add nothing), "reroute" (reroute()
     with `rounds` rounds; an assignment keeps its weight at its new expert)
     or "shared" (the dropped weights are added to the shared expert's weight
-    of 1).
+    of 1).  groups / topk_groups: group-limited routing (route()); not
+    combined with re-routing.
 
     Returns a dict with logits, idx, w, final (the expert each assignment
     ends at, -1 dropped), the dispatch fields of `final` and y[T, d]
@@ -284,11 +318,11 @@ def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
     if logits is None:
         logits = router_logits(x, W_g, b_g)
     if idx_override is None:
-        idx, w = route(logits, k)
+        idx, w = route(logits, k, groups, topk_groups)
     else:
         idx = np.asarray(idx_override, dtype=np.int32)
         w = weights_for(logits, idx)
-    final = _final_assignment(logits, idx, E, C, overflow, rounds)
+    final = _final_assignment(logits, idx, E, C, overflow, rounds, groups)
     dsp = dispatch(final, w, E, -1)
     dsp["counts"] = bincount(idx, E)  # the router's loads, before capacity
     dsp["C"] = C
@@ -312,9 +346,11 @@ def forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
     return out
 
 
-def _final_assignment(logits, idx, E, C, overflow, rounds):
+def _final_assignment(logits, idx, E, C, overflow, rounds, groups=0):
     """The expert each (token, slot) ends at under the overflow policy."""
     if overflow == "reroute":
+        if groups > 1:
+            raise ValueError("re-routing is not defined with group-limited routing")
         return reroute(logits, idx, E, C, rounds)
     if overflow not in ("drop", "shared"):
         raise ValueError(f"overflow policy {overflow!r}")
@@ -333,7 +369,8 @@ def _shared_weight(w, final, overflow):
 
 
 def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
-                   shared=None, idx_override=None, overflow="drop", rounds=0, logits=None):
+                   shared=None, idx_override=None, overflow="drop", rounds=0, logits=None,
+                   groups=0, topk_groups=0):
     """The same layer evaluated only at the given tokens.
 
     Routing, counts and capacity ranks are computed for all T tokens (a
@@ -344,11 +381,11 @@ def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
     if logits is None:
         logits = router_logits(x, W_g, b_g)
     if idx_override is None:
-        idx, w = route(logits, k)
+        idx, w = route(logits, k, groups, topk_groups)
     else:
         idx = np.asarray(idx_override, dtype=np.int32)
         w = weights_for(logits, idx)
-    final = _final_assignment(logits, idx, E, C, overflow, rounds)
+    final = _final_assignment(logits, idx, E, C, overflow, rounds, groups)
     dsp = dispatch(final, w, E, -1)
     dsp["counts"] = bincount(idx, E)
     dsp["C"] = C
@@ -372,7 +409,7 @@ def forward_tokens(tokens, x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1,
 
 
 def dense_forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None,
-                  overflow="drop", rounds=0):
+                  overflow="drop", rounds=0, groups=0, topk_groups=0):
     """Brute force for tiny inputs: run every expert on every token, then sum
     over all experts with a dense [T, E] weight that is w[t, j] where expert e
     is where token t's j-th choice ends (kept, or re-routed) and 0 elsewhere
@@ -380,7 +417,7 @@ def dense_forward(x, W_g, b_g, k, E, expert, *, kind="swiglu", C=-1, shared=None
     weighted); the shared expert's weight is 1 plus, under the "shared"
     policy, every weight left without an expert.  Must equal forward()."""
     logits = router_logits(x, W_g, b_g)
-    idx, w = route(logits, k)
+    idx, w = route(logits, k, groups, topk_groups)
     T = idx.shape[0]
     if overflow == "reroute":
         dest = reroute(logits, idx, E, C, rounds)

@@ -342,6 +342,70 @@ def test_topk_margin():
     assert oracle.topk_margin(l, 4)[0] == 0.5          # k = E: last gap skipped
 
 
+# ------------------------------------------------------------------ f4: group-limited routing
+def test_group_routing_hand_worked_examples():
+    g = _golden("group_routing_examples.json")
+    for c in g["cases"]:
+        l = np.array([c["logits"]], np.float32)
+        mask = oracle.select_groups(l, c["groups"], c["topk_groups"])
+        assert np.nonzero(mask[0])[0].tolist() == c["expected_groups"], c["name"]
+        idx, w = oracle.route(l, c["k"], c["groups"], c["topk_groups"])
+        assert idx[0].tolist() == c["expected_idx"], c["name"]
+        assert oracle.route(l, c["k"])[0][0].tolist() == c["expected_idx_without_groups"]
+        # the weights follow the ungrouped rule on the chosen experts
+        sel = l[0, idx[0]].astype(np.float64)
+        np.testing.assert_allclose(w[0], np.exp(sel) / np.exp(sel).sum(), rtol=1e-12)
+
+
+def test_group_routing_special_cases_reduce_to_plain_routing():
+    rng = np.random.default_rng(51)
+    for E, G, k in [(8, 4, 2), (16, 4, 3), (64, 8, 8), (12, 3, 5)]:
+        l = rng.integers(-3, 4, size=(200, E)).astype(np.float32)   # many ties
+        plain = oracle.route(l, k)[0]
+        # keeping every group is plain routing
+        assert np.array_equal(oracle.route(l, k, G, G)[0], plain)
+        # one expert per group, keep k groups: the groups are the experts
+        assert np.array_equal(oracle.route(l, k, E, k)[0], plain)
+
+
+def test_group_routing_brute_force_order_and_limit():
+    rng = np.random.default_rng(52)
+    T, E, G, M, k = 300, 16, 8, 3, 4
+    l = rng.integers(-4, 5, size=(T, E)).astype(np.float32)
+    mask = oracle.select_groups(l, G, M)
+    idx, w = oracle.route(l, k, G, M)
+    gs = E // G
+    for t in range(T):
+        score = [max(float(v) for v in l[t, g * gs:(g + 1) * gs]) for g in range(G)]
+        kept = [g for g in range(G) if mask[t, g]]
+        assert len(kept) == M
+        # every kept group is at least as good as every dropped one; equal
+        # scores are kept in index order
+        for g in kept:
+            for h in range(G):
+                if not mask[t, h]:
+                    assert score[g] > score[h] or (score[g] == score[h] and g < h)
+        # the experts lie in kept groups, and they are the best k of those
+        assert all(mask[t, e // gs] for e in idx[t])
+        allowed = sorted((e for e in range(E) if mask[t, e // gs]),
+                         key=lambda e: (-float(l[t, e]), e))
+        assert idx[t].tolist() == allowed[:k]
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-12)
+
+
+def test_grouped_forward_equals_dense_brute_force():
+    x, W_g, ex, sh = _tiny_swiglu(40, 8, 8, 12, seed=53, shared=True)
+    kw = dict(C=9, shared=lambda: sh, groups=4, topk_groups=2)
+    r = oracle.forward(x, W_g, None, 3, 8, lambda e: ex[e], **kw)
+    yd = oracle.dense_forward(x, W_g, None, 3, 8, lambda e: ex[e], **kw)
+    np.testing.assert_allclose(r["y"], yd, rtol=0, atol=1e-12)
+    groups_used = {(t, int(e) // 2) for t in range(40) for e in r["idx"][t]}
+    assert all(sum(1 for (t2, _) in groups_used if t2 == t) <= 2 for t in range(40))
+    with pytest.raises(ValueError):
+        oracle.forward(x, W_g, None, 3, 8, lambda e: ex[e], C=9, overflow="reroute", rounds=1,
+                       groups=4, topk_groups=2)
+
+
 # ------------------------------------------------------------------ f1: overflow policies
 def test_reroute_hand_worked_examples():
     g = _golden("reroute_examples.json")

@@ -69,7 +69,7 @@ def _traffic_from_profile(kernel_src: str, launches_bytes_key: str):
 
 
 def cpu_baseline(wl, host_experts, n_tokens: int, repeats: int, overflow="drop",
-                 rounds=0) -> dict:
+                 rounds=0, groups=0, topk_groups=0) -> dict:
     """The oracle as it stands, on the first n_tokens tokens of the workload
     (routing, dispatch, masked per-expert loop, combine; float64), run
     `repeats` times."""
@@ -82,7 +82,8 @@ def cpu_baseline(wl, host_experts, n_tokens: int, repeats: int, overflow="drop",
     for _ in range(repeats):
         oracle.forward(x, W_g, wl.b_g(), c.k, c.E, lambda e: host_experts[e], kind=c.kind,
                        C=oracle.capacity(n_tokens, c.E, c.k, c.cf),
-                       shared=wl.shared if c.shared else None, overflow=overflow, rounds=rounds)
+                       shared=wl.shared if c.shared else None, overflow=overflow, rounds=rounds,
+                       groups=groups, topk_groups=topk_groups)
     dt = time.perf_counter() - t0
     return {"value": n_tokens * repeats / dt, "unit": "tokens/s", "cores": _blas_threads(),
             "kind": "oracle",
@@ -105,6 +106,9 @@ def main() -> int:
     ap.add_argument("--overflow", default="drop", choices=("drop", "reroute", "shared"),
                     help="fate of assignments past the capacity")
     ap.add_argument("--rounds", type=int, default=1, help="re-routing rounds (--overflow reroute)")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="group-limited routing: expert groups (0 = off)")
+    ap.add_argument("--topk-groups", type=int, default=0, help="groups a token may use")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -142,7 +146,8 @@ def main() -> int:
     rounds = args.rounds if args.overflow == "reroute" else 0
     layer = moe.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff, W_g=W_g, b_g=b_g, weights=dev_w,
                          capacity=cap, kind=cfg.kind, w_dtype=cfg.w, has_shared=cfg.shared,
-                         overflow=args.overflow, reroute_rounds=rounds)
+                         overflow=args.overflow, reroute_rounds=rounds, n_groups=args.groups,
+                         topk_groups=args.topk_groups)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         layer(x)
@@ -199,6 +204,7 @@ def main() -> int:
         "config": {"workload": f"{cfg.name} MoE FFN layer", "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "top_k": cfg.k, "d_ff": cfg.d_ff, "expert": "SwiGLU", "router": "fp32",
                    "capacity": cap, "overflow": args.overflow, "reroute_rounds": rounds,
+                   "groups": args.groups, "topk_groups": args.topk_groups,
                    "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
         "layer_mfma_frac": flops_ffn / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "layer_tflops": flops_ffn / (ms_per_step * 1e-3) / 1e12,
@@ -260,7 +266,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, host_experts, args.cpu_tokens, args.cpu_repeats,
-                                              args.overflow, rounds)
+                                              args.overflow, rounds, args.groups,
+                                              args.topk_groups)
     else:
         result["cpu_baseline"] = None
 

@@ -108,6 +108,10 @@ typedef struct moe_shape {
   int32_t has_shared; /* 1: add one always-on SWIGLU shared expert (weight 1) */
   int32_t overflow;   /* moe_overflow; 0 (drop) when zero-initialised */
   int32_t reroute_rounds; /* MOE_OVERFLOW_REROUTE: re-routing rounds, 0..1024 */
+  int32_t n_groups;    /* group-limited routing: G equal groups of consecutive experts
+                          (2..64, dividing E); 0 or 1 = off */
+  int32_t topk_groups; /* groups a token may use, 1..n_groups, with
+                          top_k <= topk_groups * E / n_groups */
 } moe_shape;
 
 /* Expert weights [device].  Unused members may be NULL. */
@@ -146,6 +150,11 @@ size_t moe_workspace_bytes(const moe_shape* shape);
  * (slot 0 the largest, equal logits: the lower expert index first, -0 == +0);
  * topk_w[t, j] = exp(l_j - l_max) / sum over the kept j' of exp(l_j' - l_max),
  * i.e. softmax over all experts, keep k, divide by their sum (tutorial Q1).
+ * Group-limited routing (n_groups > 1; fde-learning "MoE 并行" Hierarchical
+ * Routing, tutorial §5 device-limited routing): a group's score is its largest
+ * logit, each token keeps its topk_groups best groups (equal scores: the lower
+ * group), and the top-k is taken among those groups' experts only; the
+ * weights follow the same rule.
  *   x [device] [T, d] (act_dtype); W_g [device] [d, E] fp32; b_g [device] [E] or NULL;
  *   logits [device] [T, E] fp32 output or NULL; topk_idx, topk_w [device] outputs;
  *   ws [device] workspace of moe_workspace_bytes(shape) bytes. */

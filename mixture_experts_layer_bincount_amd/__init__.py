@@ -46,7 +46,8 @@ class Shape(ctypes.Structure):
                 ("capacity", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("has_shared", ctypes.c_int32), ("overflow", ctypes.c_int32),
-                ("reroute_rounds", ctypes.c_int32)]
+                ("reroute_rounds", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -114,13 +115,15 @@ def _check(st):
 
 
 def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=DT_BF16,
-               kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0) -> Shape:
-    """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared")."""
+               kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0,
+               n_groups=0, topk_groups=0) -> Shape:
+    """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared").
+    n_groups / topk_groups: group-limited routing (0 = off)."""
     if isinstance(overflow, str):
         overflow = OVERFLOW[overflow]
     return Shape(int(T), int(d), int(E), int(top_k), int(d_ff), int(capacity), int(act_dtype),
                  int(w_dtype), int(kind), int(bool(has_shared)), int(overflow),
-                 int(reroute_rounds))
+                 int(reroute_rounds), int(n_groups), int(topk_groups))
 
 
 def make_weights(**tensors) -> Weights:

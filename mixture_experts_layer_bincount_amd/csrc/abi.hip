@@ -52,6 +52,19 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     return fail(MOE_ERR_INVALID, "reroute_rounds=%d must be in [0, 1024]", s->reroute_rounds);
   if (s->overflow == MOE_OVERFLOW_SHARED && !s->has_shared)
     return fail(MOE_ERR_INVALID, "overflow to the shared expert needs has_shared");
+  if (s->n_groups < 0 || s->n_groups > 64)
+    return fail(MOE_ERR_INVALID, "n_groups=%d must be in [0, 64]", s->n_groups);
+  if (s->n_groups > 1) {
+    if (s->E % s->n_groups != 0)
+      return fail(MOE_ERR_INVALID, "n_groups=%d must divide E=%d", s->n_groups, s->E);
+    if (s->topk_groups < 1 || s->topk_groups > s->n_groups)
+      return fail(MOE_ERR_INVALID, "topk_groups=%d must be in [1, n_groups]", s->topk_groups);
+    if ((int64_t)s->top_k > (int64_t)s->topk_groups * (s->E / s->n_groups))
+      return fail(MOE_ERR_INVALID, "top_k=%d exceeds the experts of topk_groups groups",
+                  s->top_k);
+    if (s->overflow == MOE_OVERFLOW_REROUTE)
+      return fail(MOE_ERR_UNSUPPORTED, "re-routing is not combined with group-limited routing");
+  }
   if (s->T * (int64_t)s->top_k > ((int64_t)1 << 31) - 1)
     return fail(MOE_ERR_INVALID, "T*top_k exceeds int32");
   if (s->kind == MOE_EXPERT_SWIGLU) {
@@ -326,6 +339,8 @@ moe_status moe_reroute(const moe_shape* shape, const float* logits, const int32_
                        int32_t* final_idx, void* ws, void* stream) {
   MOE_TRY(check_shape(shape, false));
   const moe_shape& s = *shape;
+  if (s.n_groups > 1)
+    return fail(MOE_ERR_UNSUPPORTED, "re-routing is not combined with group-limited routing");
   if (s.T == 0) return MOE_OK;
   MOE_TRY(check_ptr(logits, "logits"));
   MOE_TRY(check_ptr(topk_idx, "topk_idx"));

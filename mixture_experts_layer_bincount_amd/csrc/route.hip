@@ -221,7 +221,8 @@ template <int L, int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ partial, int splits, const float* __restrict__ b_g,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int64_t T, int E, int k, int32_t* __restrict__ cand, int KR) {
+    float* __restrict__ topk_w, int64_t T, int E, int k, int32_t* __restrict__ cand, int KR,
+    int G, int M) {
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = gt / L;
   const int sub = (int)(gt % L);
@@ -239,6 +240,28 @@ __global__ __launch_bounds__(256) void topk_kernel(
       keys[i] = topk_key(v, e);
     }
   }
+  if (G > 1) {
+    // group-limited routing: M rounds of the arg-max over the experts of the
+    // groups not yet kept; each round keeps the winner's group (the group
+    // with the best maximum; equal maxima: the lower expert, so the lower
+    // group).  Then only the kept groups' experts stay selectable.
+    const int gs = E / G;
+    int grp[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) grp[i] = min((sub + i * L) / gs, 63);  // >= G: padding, key 0
+    uint64_t kept = 0;
+    for (int m = 0; m < M; ++m) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!((kept >> grp[i]) & 1) && keys[i] > best) best = keys[i];
+      best = group_max_u64<L>(best);
+      if (best) kept |= 1ull << ((int)(0xFFFFFFFFu - (uint32_t)best) / gs);
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (!((kept >> grp[i]) & 1)) keys[i] = 0;
+  }
   int my_e = -1;
   float my_v = 0.f, vmax = 0.f;
   const int rounds = cand ? max(k, KR) : k;
@@ -249,7 +272,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     best = group_max_u64<L>(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
     const float v = key_value(best);
-    if (j == 0) vmax = v;
+    if (j == 0) vmax = v;  // the overall maximum (its group is always kept)
     if (sub == j && j < k) { my_e = e; my_v = v; }
     if (cand && live && sub == 0 && j < KR) cand[t * KR + j] = e;
     if ((e % L) == sub) {
@@ -350,7 +373,8 @@ hipError_t launch_topk(const moe_shape& s, const float* partial, int splits,
   {                                                                                        \
     const int64_t n = threads_needed * LL;                                                 \
     topk_kernel<LL, EPL><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(                     \
-        partial, splits, b_g, logits, topk_idx, topk_w, s.T, s.E, s.top_k, cand, KR);      \
+        partial, splits, b_g, logits, topk_idx, topk_w, s.T, s.E, s.top_k, cand, KR,       \
+        s.n_groups, s.topk_groups);                                                        \
     return hipGetLastError();                                                              \
   }
   if (s.E <= 1) MOE_TK(1, 1)

@@ -18,17 +18,18 @@ class MoELayer:
     weights: dict of device tensors named as in moe.h (W1, W3, W2 [, s1, s3,
     s2] [, W1s, W3s, W2s [, s1s, s3s, s2s]] for SwiGLU; W, b for Linear+bias).
     overflow: "drop", "reroute" (with reroute_rounds rounds) or "shared", the
-    fate of assignments past the capacity.
+    fate of assignments past the capacity.  n_groups / topk_groups: group-
+    limited routing (each token uses at most topk_groups groups).
     """
 
     def __init__(self, T, d, E, top_k, d_ff, *, W_g, b_g=None, weights, capacity=-1,
                  kind="swiglu", w_dtype="bf16", has_shared=False, overflow="drop",
-                 reroute_rounds=0, device="cuda"):
+                 reroute_rounds=0, n_groups=0, topk_groups=0, device="cuda"):
         self.kind = SWIGLU if kind == "swiglu" else LINEAR_BIAS
         act = DT_BF16 if self.kind == SWIGLU else DT_F32
         wdt = {"bf16": DT_BF16, "fp8_e4m3": DT_FP8_E4M3, "f32": DT_F32}[w_dtype]
         self.shape = make_shape(T, d, E, top_k, d_ff, capacity, act, wdt, self.kind, has_shared,
-                                overflow, reroute_rounds)
+                                overflow, reroute_rounds, n_groups, topk_groups)
         self.W_g = W_g
         self.b_g = b_g
         self.weights = make_weights(**weights)

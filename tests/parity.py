@@ -22,7 +22,7 @@ def oracle_capacity(cfg) -> int:
     return oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.cf)
 
 
-def gpu_forward(wl: Workload, dev=None, overflow="drop", rounds=0):
+def gpu_forward(wl: Workload, dev=None, overflow="drop", rounds=0, groups=0, topk_groups=0):
     """Run moe_forward once on the workload; returns (numpy outputs, layer, dev)."""
     import torch
 
@@ -34,7 +34,8 @@ def gpu_forward(wl: Workload, dev=None, overflow="drop", rounds=0):
     cap = moe.moe_capacity(c.T, c.E, c.k, c.cf) if c.cf else -1
     layer = moe.MoELayer(c.T, c.d, c.E, c.k, c.d_ff, W_g=dev["W_g"], b_g=dev["b_g"],
                          weights=dev["weights"], capacity=cap, kind=c.kind, w_dtype=c.w,
-                         has_shared=c.shared, overflow=overflow, reroute_rounds=rounds)
+                         has_shared=c.shared, overflow=overflow, reroute_rounds=rounds,
+                         n_groups=groups, topk_groups=topk_groups)
     layer(dev["x"])
     torch.cuda.synchronize()
     out = dict(y=layer.y.cpu().numpy(), idx=layer.topk_idx.cpu().numpy(),
@@ -81,7 +82,7 @@ def rel_err(y, y_ref) -> float:
 
 
 def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None, overflow="drop", rounds=0,
-                  decide_on=None) -> dict:
+                  decide_on=None, groups=0, topk_groups=0) -> dict:
     """Compare one moe_forward result with the oracle (on all tokens, or on
     the sampled `tokens`).  Returns a report dict.
 
@@ -96,19 +97,20 @@ def check_forward(wl: Workload, gpu: dict, tokens=None, tol=None, overflow="drop
     b_g = wl.b_g()
     logits = oracle.router_logits(x, W_g, b_g)
     if decide_on is None:
+        assert groups <= 1, "group-limited routing is checked on the GPU's logits"
         flip = check_routing(logits, c.k, gpu["idx"], gpu["w"])
         override = gpu["idx"] if flip.any() else None
     else:
         lerr = rel_err(decide_on.astype(np.float64), logits)
         assert lerr <= LOGIT_TOL, f"router logits: max-abs-err/RMS = {lerr:.3e}"
-        o_idx, o_w = oracle.route(decide_on, c.k)
+        o_idx, o_w = oracle.route(decide_on, c.k, groups, topk_groups)
         assert np.array_equal(gpu["idx"], o_idx), "top-k differs on the same fp32 logits"
         assert np.abs(gpu["w"] - o_w).max() <= 1e-5, "routing weights differ"
         logits = decide_on.astype(np.float64)
         flip = np.zeros(c.T, dtype=bool)
         override = None
     shared = wl.shared if c.shared else None
-    pol = dict(overflow=overflow, rounds=rounds)
+    pol = dict(overflow=overflow, rounds=rounds, groups=groups, topk_groups=topk_groups)
     if tokens is None:
         r = oracle.forward(x, W_g, b_g, c.k, c.E, wl.expert, kind=c.kind, C=C,
                            shared=shared, idx_override=override, logits=logits, **pol)

@@ -81,10 +81,13 @@ def test_workspace_bytes_degenerate(moe, T, d, E, k):
     (dict(d_ff=100), "d_ff"), (dict(act_dtype=0), "bf16 x"), (dict(w_dtype=0), "weights"),
     (dict(kind=7), "kind"), (dict(overflow=3), "overflow="),
     (dict(reroute_rounds=-1), "reroute_rounds"), (dict(reroute_rounds=1025), "reroute_rounds"),
-    (dict(overflow=2), "has_shared")])
+    (dict(overflow=2), "has_shared"), (dict(n_groups=3, topk_groups=1), "divide"),
+    (dict(n_groups=4, topk_groups=0), "topk_groups"), (dict(n_groups=4, topk_groups=5), "topk_groups"),
+    (dict(n_groups=8, topk_groups=1, top_k=2), "top_k"), (dict(n_groups=65, topk_groups=1), "n_groups"),
+    (dict(n_groups=4, topk_groups=2, overflow=1, capacity=4), "re-routing")])
 def test_validation_rejects_bad_shapes(moe, kw, needle):
     base = dict(T=16, d=256, E=8, top_k=2, d_ff=128, capacity=-1, act_dtype=1, w_dtype=1,
-                kind=1, has_shared=False, overflow=0, reroute_rounds=0)
+                kind=1, has_shared=False, overflow=0, reroute_rounds=0, n_groups=0, topk_groups=0)
     base.update(kw)
     s = moe.make_shape(**base)
     fake = 256  # never dereferenced: validation fails first

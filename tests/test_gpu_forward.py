@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from moe_synth import Workload, custom_config, get_config
-from tests.parity import check_forward, gpu_forward, rel_err
+from tests.parity import check_forward, gpu_forward, gpu_logits, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,35 @@ def test_workload_full_size(moe, name, nsample):
     toks = None if nsample >= wl.cfg.T else _sample_tokens(wl.cfg.T, nsample, seed=1)
     rep = check_forward(wl, out, tokens=toks)
     print(f"  err={rep['err']:.3e} flipped={rep['flipped']} kept={rep['kept']}", flush=True)
+
+
+@pytest.mark.parametrize("T,d,E,k,d_ff,cf,shared,w,G,M", [
+    (600, 256, 16, 4, 256, None, False, "bf16", 4, 2),
+    (500, 512, 32, 6, 128, 1.25, True, "bf16", 8, 3),
+    (300, 256, 64, 8, 128, None, True, "fp8_e4m3", 8, 4)])
+def test_forward_group_limited(moe, T, d, E, k, d_ff, cf, shared, w, G, M):
+    """Group-limited routing end to end; routing decided on the GPU's fp32
+    logits on both sides (the logits checked against the oracle's)."""
+    print(f"[forward groups] T={T} E={E} k={k} G={G} M={M} cf={cf} shared={shared} w={w}",
+          flush=True)
+    cfg = custom_config(T, d, E, k, d_ff, w=w, cf=cf, shared=shared, seed=T + 5 * E)
+    wl = Workload(cfg)
+    out, layer, dev = gpu_forward(wl, groups=G, topk_groups=M)
+    gl = gpu_logits(layer, dev)
+    rep = check_forward(wl, out, decide_on=gl, groups=G, topk_groups=M)
+    idx = out["idx"]
+    assert all(len({int(e) // (E // G) for e in row}) <= M for row in idx)
+    print(f"  err={rep['err']:.3e} kept={rep['kept']}", flush=True)
+
+
+def test_fine_grained_group_limited_full_size(moe):
+    """The 256-expert layer (k = 8 + a shared expert) with 8 groups of 32
+    experts and at most 4 groups per token, at full size."""
+    print("[workload] fine_grained, 8 groups, top-4 groups", flush=True)
+    wl = Workload(get_config("fine_grained"))
+    out, layer, dev = gpu_forward(wl, groups=8, topk_groups=4)
+    gl = gpu_logits(layer, dev)
+    rep = check_forward(wl, out, tokens=_sample_tokens(wl.cfg.T, 12, seed=3), decide_on=gl,
+                        groups=8, topk_groups=4)
+    print(f"  err={rep['err']:.3e} kept={rep['kept']}", flush=True)
+

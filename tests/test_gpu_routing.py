@@ -4,11 +4,15 @@ Routing from given logits and dispatch from given selections must be
 bit-exact; the fused router may only change the selection of tokens whose
 top-k margin is below 1e-5.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
 import oracle
 from moe_synth import Workload, custom_config
+from tests.conftest import GOLDEN
 from tests.parity import check_routing
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +141,36 @@ def test_dispatch_bit_exact(moe, T, E, k, C, skew):
     assert np.array_equal(perm_w.cpu().numpy()[:P], r["perm_w"].astype(np.float32))
     xp = x_perm.cpu().numpy().view(np.uint16)[:P]
     assert np.array_equal(xp, x[r["perm_token"]])
+
+
+@pytest.mark.parametrize("T,E,G,M,k,ties", [
+    (500, 8, 4, 2, 3, True), (700, 64, 8, 3, 6, True), (300, 256, 8, 4, 8, True),
+    (1000, 256, 8, 4, 8, False), (129, 1024, 64, 5, 32, True), (77, 12, 3, 1, 4, True),
+    (64, 16, 16, 2, 2, True), (1, 32, 4, 4, 8, False), (4096, 8, 2, 1, 2, False)])
+def test_group_limited_route_bit_exact(moe, T, E, G, M, k, ties):
+    """Group-limited selection from given logits equals the oracle's bit for bit."""
+    print(f"[group route] T={T} E={E} G={G} M={M} k={k} ties={ties}", flush=True)
+    l = _logits(T, E, seed=7 * T + E + G, ties=ties)
+    s = moe.make_shape(T, 256, E, k, n_groups=G, topk_groups=M)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route_from_logits(s, torch.from_numpy(l).cuda(), idx, w)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route(l, k, G, M)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=0, atol=1e-6)
+
+
+def test_group_limited_route_hand_worked(moe):
+    with open(os.path.join(GOLDEN, "group_routing_examples.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        l = np.array([c["logits"]], np.float32)
+        s = moe.make_shape(1, 256, c["E"], c["k"], n_groups=c["groups"],
+                           topk_groups=c["topk_groups"])
+        idx = torch.empty((1, c["k"]), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, c["k"]), dtype=torch.float32, device="cuda")
+        moe.moe_route_from_logits(s, torch.from_numpy(l).cuda(), idx, w)
+        torch.cuda.synchronize()
+        assert idx.cpu().numpy()[0].tolist() == c["expected_idx"], c["name"]
+

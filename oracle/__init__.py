@@ -28,6 +28,9 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
                        overflow-to-shared closed form)
   stats (imbalance, LPT, naive split, variance)   pinned (tutorial §3.3 / §6 values,
                        4/3 bound against brute-force OPT)
+  replicate / eplb_plan   pinned (no replicas = the tutorial's LPT, hand-worked
+                       cases in tests/golden, the D'Hondt highest-quotient
+                       statement of the replication, placement invariants)
   fp8 e4m3 decode      pinned (OCP format values, torch float8_e4m3fn)
   full-size workloads  parity unpinned beyond the invariants above (the pages
                        print no outputs for those shapes)
@@ -37,5 +40,6 @@ from .moe_oracle import (  # noqa: F401
     bincount, capacity, capacity_ranks, dispatch, reroute, silu, expert_linear_bias,
     expert_swiglu, forward, forward_tokens, dense_forward, topk_margin,
 )
-from .stats import expert_imbalance, lpt_pack, naive_split, sample_variance  # noqa: F401
+from .stats import (expert_imbalance, lpt_pack, naive_split, sample_variance,  # noqa: F401
+                    replicate, replica_loads, eplb_plan)
 from .fp8 import e4m3_decode_table, dequant_rows  # noqa: F401

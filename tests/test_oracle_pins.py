@@ -342,6 +342,67 @@ def test_topk_margin():
     assert oracle.topk_margin(l, 4)[0] == 0.5          # k = E: last gap skipped
 
 
+# ------------------------------------------------------------------ f3: replication + placement
+def test_eplb_hand_worked_examples():
+    g = _golden("eplb_replication_examples.json")
+    for c in g["cases"]:
+        p = oracle.eplb_plan(c["load"], c["devices"], c["extra"])
+        assert p["replicas"].tolist() == c["replicas"], c["name"]
+        assert p["slot_load"].tolist() == c["slot_load"], c["name"]
+        assert p["slot_device"].tolist() == c["slot_device"], c["name"]
+        assert p["device_load"].tolist() == c["device_load"], c["name"]
+        p0 = oracle.eplb_plan(c["load"], c["devices"], 0)
+        assert p0["device_load"].tolist() == c["device_load_without_replicas"], c["name"]
+
+
+def test_eplb_without_replicas_is_the_tutorial_lpt():
+    g = _golden("lpt_example.json")
+    p = oracle.eplb_plan(g["load"], g["devices"], 0)
+    assert p["slot_device"].tolist() == g["lpt_assignment"]
+    assert p["device_load"].tolist() == g["lpt_device_load"]
+    rng = np.random.default_rng(61)
+    for E, D in [(8, 3), (64, 8), (256, 8), (5, 7)]:
+        load = rng.integers(0, 400, size=E)
+        load[rng.integers(0, E)] = 0
+        a, dev = oracle.lpt_pack(load, D)
+        p = oracle.eplb_plan(load, D, 0)
+        assert np.array_equal(p["slot_device"], a) and np.array_equal(p["device_load"], dev)
+
+
+def _dhondt(load, D, extra):
+    """The replication stated as a highest-quotient apportionment: the extra
+    replicas are the `extra` largest quotients load_e / j (j = 1 .. D-1, the
+    quotient that earns replica j + 1), ordered by (-quotient, expert, j)."""
+    from fractions import Fraction
+    q = sorted(((Fraction(int(l), j), e, j) for e, l in enumerate(load) for j in range(1, D)),
+               key=lambda v: (-v[0], v[1], v[2]))
+    r = [1] * len(load)
+    for _, e, _ in q[:extra]:
+        r[e] += 1
+    return r
+
+
+@pytest.mark.parametrize("E,D,extra", [(8, 4, 3), (64, 8, 16), (256, 8, 32), (16, 2, 40),
+                                       (6, 3, 20), (32, 8, 0)])
+def test_eplb_replication_and_placement_invariants(E, D, extra):
+    rng = np.random.default_rng(E * 7 + D + extra)
+    load = (rng.zipf(1.6, size=E) * 10).clip(0, 5000)
+    load[rng.integers(0, E)] = 0
+    p = oracle.eplb_plan(load, D, extra)
+    r = p["replicas"]
+    assert r.tolist() == _dhondt(load, D, extra)
+    assert r.sum() == E + min(extra, E * (D - 1)) and r.max() <= D
+    # every expert's tokens are split over its replicas, evenly
+    for e in range(E):
+        sl = p["slot_load"][p["slot_expert"] == e]
+        assert sl.sum() == load[e] and sl.max() - sl.min() <= 1
+        devs = p["slot_device"][p["slot_expert"] == e]
+        assert len(set(devs.tolist())) == devs.size      # copies on distinct devices
+    assert p["device_load"].sum() == load.sum()
+    for d in range(D):
+        assert p["device_load"][d] == p["slot_load"][p["slot_device"] == d].sum()
+
+
 # ------------------------------------------------------------------ f4: group-limited routing
 def test_group_routing_hand_worked_examples():
     g = _golden("group_routing_examples.json")

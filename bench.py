@@ -236,6 +236,28 @@ def main() -> int:
                        "lpt_8_max_over_mean": max(bins) / (sum(bins) / len(bins))}
     result["load_stats"] = stats
 
+    # ---- online EPLB on the device: replicas + placement onto 8 devices from
+    # this step's counts (still on the device), E/8 extra replicas
+    D, extra = 8, max(1, cfg.E // 8)
+    reps = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    sdev = torch.empty(cfg.E + extra, dtype=torch.int32, device="cuda")
+    sload = torch.empty(cfg.E + extra, dtype=torch.int32, device="cuda")
+    dload = torch.empty(D, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        moe.moe_eplb_plan(layer.counts, D, extra, reps, sdev, sload, dload)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        moe.moe_eplb_plan(layer.counts, D, extra, reps, sdev, sload, dload)
+    e1.record()
+    torch.cuda.synchronize()
+    dl = dload.cpu().numpy()
+    result["eplb_plan"] = {"devices": D, "extra_replicas": extra,
+                           "us_per_plan": e0.elapsed_time(e1) / 20 * 1e3,
+                           "device_load_max_over_mean": float(dl.max() / dl.mean()),
+                           "without_replicas_max_over_mean": stats["counts"]["lpt_8_max_over_mean"]}
+
     # ---- decode-shaped layer: the same weights, the first 64 tokens
     if not args.no_decode and cfg.name == "mixtral":
         dcfg = get_config("decode")

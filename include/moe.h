@@ -273,6 +273,32 @@ double moe_load_imbalance(const int64_t* load, int32_t E);
 moe_status moe_lpt_pack(const int64_t* load, int32_t E, int32_t D,
                         int32_t* assignment, int64_t* bin_load);
 
+/* Expert placement with hot-expert replication, on the device (fde-learning
+ * "MoE 并行" Expert 复制: a popular expert gets a copy on several GPUs; tutorial
+ * §3.3 / §4.3 LPT packing, §5 online EPLB).  From the per-expert loads:
+ *   1. each expert has one replica; each of `extra` more goes to the expert
+ *      with the largest load per replica (equal: the lower expert), at most D
+ *      replicas per expert;
+ *   2. an expert's load splits evenly over its replicas (the first load % r
+ *      take one more); slot s numbers the replicas expert by expert;
+ *   3. LPT over the slots: heaviest first (equal: lower expert, then lower
+ *      replica), each to the lightest device that holds no copy of the same
+ *      expert yet (equal: lower device).
+ * With extra = 0 this is moe_lpt_pack.  Runs as one kernel on `stream`: the
+ * loads can be moe_forward's counts of the same step, with no host round trip.
+ *   counts      [device] int32 [E] loads, >= 0; E in [1, 1024]
+ *   D           devices, 1..64;  extra  replicas beyond E, 0..1024, E + extra <= 2048
+ *   replicas    [device] int32 [E] output
+ *   slot_device [device] int32 [E + extra] output: device of slot s, -1 for
+ *               unused slots (when every expert already has D replicas)
+ *   slot_load   [device] int32 [E + extra] output: the slot's share of its
+ *               expert's load (0 for unused slots)
+ *   device_load [device] int64 [D] output
+ * MOE_ERR_INVALID for sizes out of range or NULL pointers. */
+moe_status moe_eplb_plan(const int32_t* counts, int32_t E, int32_t D, int32_t extra,
+                         int32_t* replicas, int32_t* slot_device, int32_t* slot_load,
+                         int64_t* device_load, void* stream);
+
 /* Stage timing, for profiling.  While enabled, moe_forward records a HIP event
  * on its stream before its first kernel and after each stage: 0 router GEMM,
  * 1 top-k, 2 dispatch (histogram, scan, rank), 3 clearing y, 4 grouped

@@ -30,7 +30,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_E
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_from_logits",
            "moe_reroute", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_load_imbalance", "moe_lpt_pack", "moe_timing_enable", "moe_timing_collect",
+           "moe_load_imbalance", "moe_lpt_pack", "moe_eplb_plan", "moe_timing_enable",
+           "moe_timing_collect",
            "moe_timing_stage_name", "moe_last_error")
 
 
@@ -81,6 +82,9 @@ _lib.moe_load_imbalance.argtypes = [_P(ctypes.c_int64), ctypes.c_int32]
 _lib.moe_lpt_pack.restype = ctypes.c_int
 _lib.moe_lpt_pack.argtypes = [_P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32,
                               _P(ctypes.c_int32), _P(ctypes.c_int64)]
+_lib.moe_eplb_plan.restype = ctypes.c_int
+_lib.moe_eplb_plan.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
+                               _vp, _vp]
 _lib.moe_timing_enable.restype = ctypes.c_int
 _lib.moe_timing_enable.argtypes = [ctypes.c_int]
 _lib.moe_timing_collect.restype = ctypes.c_int
@@ -217,6 +221,13 @@ def moe_expert_ffn(shape, weights, x, offsets, perm_token, perm_w, y_perm, y, ws
 def moe_combine(shape, y_perm, slot_pos, topk_w, y, stream=None):
     _check(_lib.moe_combine(ctypes.byref(shape), _ptr(y_perm), _ptr(slot_pos), _ptr(topk_w),
                             _ptr(y), _stream(stream)))
+
+
+def moe_eplb_plan(counts, D, extra, replicas, slot_device, slot_load, device_load, stream=None):
+    """Device-side replication + placement from the int32 counts tensor [E]."""
+    _check(_lib.moe_eplb_plan(_ptr(counts), int(counts.numel()), int(D), int(extra),
+                              _ptr(replicas), _ptr(slot_device), _ptr(slot_load),
+                              _ptr(device_load), _stream(stream)))
 
 
 def moe_forward(shape, x, W_g, b_g, weights, y, topk_idx, topk_w, counts, offsets, ws,

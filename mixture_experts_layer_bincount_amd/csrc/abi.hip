@@ -544,6 +544,23 @@ moe_status moe_lpt_pack(const int64_t* load, int32_t E, int32_t D, int32_t* assi
   return MOE_OK;
 }
 
+moe_status moe_eplb_plan(const int32_t* counts, int32_t E, int32_t D, int32_t extra,
+                         int32_t* replicas, int32_t* slot_device, int32_t* slot_load,
+                         int64_t* device_load, void* stream) {
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID, "E=%d must be in [1, 1024]", E);
+  if (D < 1 || D > 64) return fail(MOE_ERR_INVALID, "D=%d must be in [1, 64]", D);
+  if (extra < 0 || extra > 1024 || E + extra > 2048)
+    return fail(MOE_ERR_INVALID, "extra=%d must be in [0, 1024] with E + extra <= 2048", extra);
+  MOE_TRY(check_ptr(counts, "counts"));
+  MOE_TRY(check_ptr(replicas, "replicas"));
+  MOE_TRY(check_ptr(slot_device, "slot_device"));
+  MOE_TRY(check_ptr(slot_load, "slot_load"));
+  MOE_TRY(check_ptr(device_load, "device_load", 8));
+  return hip_status(launch_eplb_plan(counts, E, D, extra, replicas, slot_device, slot_load,
+                                     device_load, (hipStream_t)stream),
+                    "eplb plan");
+}
+
 moe_status moe_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
   g_timing = on != 0;

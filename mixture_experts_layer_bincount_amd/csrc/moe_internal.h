@@ -111,6 +111,10 @@ hipError_t launch_reroute(const moe_shape& s, const WsLayout& L, const int32_t* 
 // shared_w[t] = 1 + sum of the token's dropped topk_w (slot_pos == -1).
 hipError_t launch_shared_weights(const moe_shape& s, const int32_t* slot_pos,
                                  const float* topk_w, float* shared_w, hipStream_t st);
+// One workgroup: replication, slot loads, LPT placement (see moe_eplb_plan).
+hipError_t launch_eplb_plan(const int32_t* counts, int E, int D, int extra, int32_t* replicas,
+                            int32_t* slot_device, int32_t* slot_load, int64_t* device_load,
+                            hipStream_t st);
 hipError_t launch_gather(const moe_shape& s, int64_t P_max, const int32_t* offsets,
                          const int32_t* perm_token, const void* x, void* x_perm,
                          hipStream_t st);

@@ -131,3 +131,12 @@ def test_workspace_covers_rerouting(moe):
                                                  overflow="reroute", reroute_rounds=99))
     assert r99 - base < 4096 * 64 * 4 + 4096   # capped at E candidates
 
+
+@pytest.mark.parametrize("E,D,extra,needle", [(0, 8, 0, "E="), (1025, 8, 0, "E="), (8, 0, 0, "D="),
+                                              (8, 65, 0, "D="), (8, 4, -1, "extra"),
+                                              (1024, 8, 1025, "extra"), (1500, 8, 600, "E=")])
+def test_eplb_plan_validation(moe, E, D, extra, needle):
+    fake = 256  # never dereferenced: validation fails first
+    st = moe._lib.moe_eplb_plan(fake, E, D, extra, fake, fake, fake, fake, 0)
+    assert st == 1 and needle in moe.moe_last_error()
+

@@ -583,13 +583,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // 16-byte chunk; the B tile rows are 32-aligned as well
   const int swzb = FP8 ? (frow / C::RPSB) % C::CPRB : 0;
   // step boundary before slice sl (sl % HPS == 0, sl > 0): see above
+  // a wave's DMA instructions per step: NI (activation waves) or NIB (weight
+  // waves; fewer with fp8 weights), so "k steps still in flight" is a
+  // different count per wave kind
+  auto wait_steps = [&](auto KS) __attribute__((always_inline)) {
+    constexpr int k = decltype(KS)::value;
+    if (a_wave)
+      wait_vmcnt<k * C::NI>();
+    else
+      wait_vmcnt<k * C::NIB>();
+  };
   auto step_sync = [&](int sl) __attribute__((always_inline)) {
     const int t = sl / HPS;
     wait_lgkm0();
     // steady state: the NS - 2 later steps may stay in flight; near the end
     // (fewer issued) wait for everything
     if (t + NS - 2 <= nk - 1)
-      wait_vmcnt<(NS - 2) * C::NI>();
+      wait_steps(std::integral_constant<int, NS - 2>{});
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -668,9 +678,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       if (s < nk) issue(s, s);
     });
     if (NS - 2 >= 2 && nk > 2)
-      wait_vmcnt<2 * C::NI>();
+      wait_steps(std::integral_constant<int, 2>{});
     else if (NS - 2 >= 1 && nk > 1)
-      wait_vmcnt<C::NI>();
+      wait_steps(std::integral_constant<int, 1>{});
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();

@@ -104,6 +104,125 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
+// Up to 64 experts: every wave covers all of them for its own 64 rows (the
+// activations are read once), and the four waves share each 32-deep step of
+// the split weights through LDS.  The step's 3 x 16*NJ weight rows are
+// loaded cooperatively (16 bytes per thread and chunk) and stored in
+// fragment order (fragment f = part * NJ + expert tile, lane-major), so a
+// wave's fragment read is 64 consecutive 16-byte pieces.  Two LDS buffers:
+// step s + 1 is loaded into registers while step s is computed, then
+// written to the other buffer; one barrier per step.
+template <int NJ>
+__global__ __launch_bounds__(256) void router_lds_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ Wp,
+                                                         float* __restrict__ partial, int64_t T,
+                                                         int d, int E, int E_pad, int ksteps_per) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  constexpr int EP = 16 * NJ;
+  constexpr int CHUNKS = 3 * EP * 4;                 // 16-byte chunks of one step
+  constexpr int CPT = (CHUNKS + 255) / 256;          // per thread
+  constexpr int BUF = 3 * NJ * 1024;                 // bytes of one step in LDS
+  __shared__ __attribute__((aligned(16))) char sb[2][BUF];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  const int split = blockIdx.y;
+  const int k0 = split * ksteps_per * 32;
+  const int k1 = min(d, k0 + ksteps_per * 32);  // an empty last split stores zeros
+  const int nsteps = k1 > k0 ? (k1 - k0) / 32 : 0;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = min(r0 + i * 16 + fr, T - 1);
+    arow[i] = x + t * d + fk;
+  }
+  const int64_t plane = (int64_t)E_pad * d;
+  // this thread's weight chunks: global source and LDS destination
+  int bsrc[CPT];  // element offsets into Wp (3 * E_pad * d < 2^31)
+  int bdst[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int q = tid + c * 256;
+    const int kc = q & 3, pe = q >> 2;           // (part, expert) row, K chunk
+    const int part = pe / EP, e = pe % EP;
+    bsrc[c] = (int)(part * plane + (int64_t)e * d + kc * 8);
+    bdst[c] = (part * NJ + e / 16) * 1024 + (kc * 16 + e % 16) * 16;
+  }
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // (the staged chunks live in a local array of each step, fully unrolled,
+  // so they stay in registers)
+  auto load_b = [&](int k, uint4 (&breg)[CPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      breg[c] = (CHUNKS % 256 == 0 || tid + c * 256 < CHUNKS)
+                    ? *(const uint4*)(Wp + bsrc[c] + k) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_b = [&](int buf, const uint4 (&breg)[CPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (CHUNKS % 256 == 0 || tid + c * 256 < CHUNKS) *(uint4*)(sb[buf] + bdst[c]) = breg[c];
+  };
+  auto load_a = [&](int k, bf16x8_t (&a)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(arow[i] + k);
+  };
+  auto step = [&](int s, bf16x8_t (&a)[4], bf16x8_t (&an)[4]) __attribute__((always_inline)) {
+    const bool more = s + 1 < nsteps;
+    uint4 breg[CPT];
+    if (more) {
+      load_b(k0 + (s + 1) * 32, breg);
+      load_a(k0 + (s + 1) * 32, an);
+    }
+    const char* buf = sb[s & 1];
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8_t b = *(const bf16x8_t*)(buf + (part * NJ + j) * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    if (more) store_b((s + 1) & 1, breg);
+    __syncthreads();
+  };
+  if (nsteps > 0) {
+    bf16x8_t a0[4], a1[4];
+    {
+      uint4 breg[CPT];
+      load_b(k0, breg);
+      store_b(0, breg);
+    }
+    load_a(k0, a0);
+    __syncthreads();
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+      step(s, a0, a1);
+      step(s + 1, a1, a0);
+    }
+    if (s < nsteps) step(s, a0, a1);
+  }
+  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert j*16 + lane%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = r0 + i * 16 + (lane >> 4) * 4 + r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = j * 16 + fr;
+        if (e < E) partial[((int64_t)split * T + t) * E + e] = acc[i][j][r];
+      }
+    }
+}
+
 // Workgroup of 4 waves: WE waves along the experts (each 16*NJ of them) and
 // 4/WE along the tokens (64 rows each), so a wave's tile stays small enough
 // to double-buffer its operand fragments.  Fragments (16 bytes per lane: row
@@ -319,9 +438,10 @@ size_t router_split_bytes(const moe_shape& s) {
   return ep ? (size_t)3 * ep * s.d * sizeof(uint16_t) : 0;
 }
 
-// Waves along the experts in the MFMA router: as many as 16-expert tiles
-// allow, up to the workgroup's 4.
-static int router_we(int ep) { return std::min(4, ep / 16); }
+// Waves along the experts in the MFMA router.  Up to 64 experts one wave
+// covers them all (each activation row is then read once); beyond that,
+// 64 experts per wave.
+static int router_we(int ep) { return ep <= 64 ? 1 : ep / 64; }
 
 int router_splits_for(const moe_shape& s) {
   const int ep = router_mfma_epad(s);
@@ -356,7 +476,15 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_
                                                      s.E, ep, per);                               \
     return hipGetLastError();                                                                     \
   }
-    MOE_RM(16, 1, 1) MOE_RM(32, 1, 2) MOE_RM(64, 1, 4) MOE_RM(128, 2, 4) MOE_RM(256, 4, 4)
+#define MOE_RL(EP, NJ)                                                                            \
+  if (ep == EP) {                                                                                 \
+    router_lds_kernel<NJ><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d, s.E,  \
+                                                ep, per);                                         \
+    return hipGetLastError();                                                                     \
+  }
+    MOE_RL(16, 1) MOE_RL(32, 2) MOE_RL(64, 4)
+#undef MOE_RL
+    MOE_RM(128, 4, 2) MOE_RM(256, 4, 4)
 #undef MOE_RM
     return hipErrorInvalidValue;
   }

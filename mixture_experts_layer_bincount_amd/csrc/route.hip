@@ -7,7 +7,7 @@
 // made on the logits (softmax is monotone), ties to the lower expert index.
 //
 // Stage A: split-K partial dot products written to partial[split][t][e].
-//   bf16 activations (router_split_kernel + router_mfma_kernel): the fp32
+//   bf16 activations (router_split_kernel + router_lds_kernel): the fp32
 //   gate is split exactly into three bf16 parts and contracted on bf16 MFMA
 //   with fp32 accumulation (fp32-GEMM accuracy at matrix-core speed).
 //   fp32 activations (router_gemm_kernel): one workgroup = 64 tokens x all
@@ -104,9 +104,10 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
-// Up to 64 experts: every wave covers all of them for its own 64 rows (the
-// activations are read once), and the four waves share each 32-deep step of
-// the split weights through LDS.  The step's 3 x 16*NJ weight rows are
+// Blocks of up to 64 experts: every wave covers the block's experts for its
+// own 64 rows (with at most 64 experts the activations are read once), and
+// the four waves share each 32-deep step of the split weights through LDS;
+// blockIdx.z selects the 64-expert block.  The step's 3 x 16*NJ weight rows are
 // loaded cooperatively (16 bytes per thread and chunk) and stored in
 // fragment order (fragment f = part * NJ + expert tile, lane-major), so a
 // wave's fragment read is 64 consecutive 16-byte pieces.  Two LDS buffers:
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(256) void router_lds_kernel(const uint16_t* __restr
   const int k1 = min(d, k0 + ksteps_per * 32);  // an empty last split stores zeros
   const int nsteps = k1 > k0 ? (k1 - k0) / 32 : 0;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const int eb = blockIdx.z * EP;  // first expert of the block
   const uint16_t* arow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256) void router_lds_kernel(const uint16_t* __restr
     const int q = tid + c * 256;
     const int kc = q & 3, pe = q >> 2;           // (part, expert) row, K chunk
     const int part = pe / EP, e = pe % EP;
-    bsrc[c] = (int)(part * plane + (int64_t)e * d + kc * 8);
+    bsrc[c] = (int)(part * plane + (int64_t)(eb + e) * d + kc * 8);
     bdst[c] = (part * NJ + e / 16) * 1024 + (kc * 16 + e % 16) * 16;
   }
   f32x4 acc[4][NJ];
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256) void router_lds_kernel(const uint16_t* __restr
     }
     if (s < nsteps) step(s, a0, a1);
   }
-  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert j*16 + lane%16
+  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert eb + j*16 + lane%16
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -217,89 +219,7 @@ __global__ __launch_bounds__(256) void router_lds_kernel(const uint16_t* __restr
       if (t >= T) continue;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int e = j * 16 + fr;
-        if (e < E) partial[((int64_t)split * T + t) * E + e] = acc[i][j][r];
-      }
-    }
-}
-
-// Workgroup of 4 waves: WE waves along the experts (each 16*NJ of them) and
-// 4/WE along the tokens (64 rows each), so a wave's tile stays small enough
-// to double-buffer its operand fragments.  Fragments (16 bytes per lane: row
-// lane%16, K chunk lane/16) are read straight from global memory, the next
-// 32-deep step's while the current step's 16x16x32 MFMAs run; the
-// workgroup's K range is one split of the reduction.
-template <int NJ, int WE>
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ Wp,
-                                                          float* __restrict__ partial, int64_t T,
-                                                          int d, int E, int E_pad, int ksteps_per) {
-  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-  constexpr int WM = 4 / WE;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int we = wave % WE, wm = wave / WE;
-  const int64_t r0 = (int64_t)blockIdx.x * (64 * WM) + wm * 64;
-  const int e0 = we * NJ * 16;
-  const int split = blockIdx.y;
-  const int k0 = split * ksteps_per * 32;
-  const int k1 = min(d, k0 + ksteps_per * 32);  // an empty last split stores zeros
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const uint16_t* arow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = min(r0 + i * 16 + fr, T - 1);
-    arow[i] = x + t * d + fk;
-  }
-  const int64_t plane = (int64_t)E_pad * d;
-  const uint16_t* brow = Wp + (int64_t)(e0 + fr) * d + fk;
-  f32x4 acc[4][NJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int k, bf16x8_t (&a)[4], bf16x8_t (&b)[3][NJ]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t*)(arow[i] + k);
-#pragma unroll
-    for (int part = 0; part < 3; ++part)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        b[part][j] = *(const bf16x8_t*)(brow + part * plane + (int64_t)j * 16 * d + k);
-  };
-  auto mma = [&](bf16x8_t (&a)[4], bf16x8_t (&b)[3][NJ]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int part = 0; part < 3; ++part)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[part][j], acc[i][j], 0, 0, 0);
-  };
-  // two steps per iteration, fragments of the next step loaded under the
-  // current one's MFMAs (a reload past the end rereads the last step, unused)
-  if (k0 < k1) {
-    bf16x8_t a0[4], b0[3][NJ], a1[4], b1[3][NJ];
-    load(k0, a0, b0);
-    int k = k0;
-    for (; k + 64 <= k1; k += 64) {
-      load(k + 32, a1, b1);
-      mma(a0, b0);
-      load(min(k + 64, k1 - 32), a0, b0);
-      mma(a1, b1);
-    }
-    if (k < k1) mma(a0, b0);
-  }
-  // acc[i][j][r]: row i*16 + (lane/16)*4 + r, expert e0 + j*16 + lane%16
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = r0 + i * 16 + (lane >> 4) * 4 + r;
-      if (t >= T) continue;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int e = e0 + j * 16 + fr;
+        const int e = eb + j * 16 + fr;
         if (e < E) partial[((int64_t)split * T + t) * E + e] = acc[i][j][r];
       }
     }
@@ -438,17 +358,14 @@ size_t router_split_bytes(const moe_shape& s) {
   return ep ? (size_t)3 * ep * s.d * sizeof(uint16_t) : 0;
 }
 
-// Waves along the experts in the MFMA router.  Up to 64 experts one wave
-// covers them all (each activation row is then read once); beyond that,
-// 64 experts per wave.
-static int router_we(int ep) { return ep <= 64 ? 1 : ep / 64; }
+// Expert blocks of the MFMA router (64 experts each beyond 64).
+static int router_eblocks(int ep) { return ep <= 64 ? 1 : ep / 64; }
 
 int router_splits_for(const moe_shape& s) {
   const int ep = router_mfma_epad(s);
   if (ep) {
     // about 512 workgroups (2048 waves), K pieces of at least 8 steps of 32
-    const int rows_per_wg = 64 * (4 / router_we(ep));
-    const int64_t wgs = std::max<int64_t>(1, (s.T + rows_per_wg - 1) / rows_per_wg);  // T may be 0
+    const int64_t wgs = std::max<int64_t>(1, (s.T + 255) / 256) * router_eblocks(ep);  // T may be 0
     const int ksteps = s.d / 32;
     const int64_t want = (512 + wgs - 1) / wgs;
     return (int)std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, ksteps / 8)));
@@ -468,24 +385,15 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_
         W_g, s.d, s.E, ep, Wp);
     const int ksteps = s.d / 32;
     const int per = (ksteps + splits - 1) / splits;
-    const int rows_per_wg = 64 * (4 / router_we(ep));
-    dim3 grid((unsigned)((s.T + rows_per_wg - 1) / rows_per_wg), (unsigned)splits);
-#define MOE_RM(EP, NJ, WE)                                                                        \
-  if (ep == EP) {                                                                                 \
-    router_mfma_kernel<NJ, WE><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d,   \
-                                                     s.E, ep, per);                               \
-    return hipGetLastError();                                                                     \
-  }
+    dim3 grid((unsigned)((s.T + 255) / 256), (unsigned)splits, (unsigned)router_eblocks(ep));
 #define MOE_RL(EP, NJ)                                                                            \
   if (ep == EP) {                                                                                 \
     router_lds_kernel<NJ><<<grid, 256, 0, st>>>((const uint16_t*)x, Wp, partial, s.T, s.d, s.E,  \
                                                 ep, per);                                         \
     return hipGetLastError();                                                                     \
   }
-    MOE_RL(16, 1) MOE_RL(32, 2) MOE_RL(64, 4)
+    MOE_RL(16, 1) MOE_RL(32, 2) MOE_RL(64, 4) MOE_RL(128, 4) MOE_RL(256, 4)
 #undef MOE_RL
-    MOE_RM(128, 4, 2) MOE_RM(256, 4, 4)
-#undef MOE_RM
     return hipErrorInvalidValue;
   }
   if (s.act_dtype == MOE_DT_F32)

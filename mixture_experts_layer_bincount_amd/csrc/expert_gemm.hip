@@ -87,8 +87,6 @@ struct GemmParams {
   float* tail_slab;           // MODE_DOWN_PERM: fp32 partial tiles of split tail tiles
   int tail_cap;               //   (room for tail_cap tiles of 64 Ki floats)
   int group_n;                // weight tiles per expert-aligned block of the tile order
-  int krot;                   // rotate each workgroup's K order (spreads L2 channels)
-  int cache_aux;              // cache-policy bits of the operand loads
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -98,18 +96,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     if (lane >= off) v += o;
   }
   return v;
-}
-
-// fp8 e4m3 (OCP) -> bf16 bits, exact and branch-free.  Normal codes move
-// exponent and mantissa fields (bias 7 -> 127); subnormal codes (exponent
-// field 0) are m * 2^-9, formed exactly in fp32 and truncated to bf16 (at
-// most 3 significant bits, so nothing is lost).
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8;
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  const uint32_t normal = ((e + 120u) << 7) | (m << 4);
-  const uint32_t sub = __float_as_uint((float)m * 0x1p-9f) >> 16;
-  return s | (e ? normal : sub);
 }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at
@@ -132,30 +118,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* ptr, 
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
                                            __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// 8 weight elements as bf16 bits: 16 bytes of bf16, or 8 fp8 codes widened.
-template <bool FP8>
-__device__ __forceinline__ uint4 load_b8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  if constexpr (!FP8) {
-    return buf_load16(r, voff, soff);
-  } else {
-    const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    uint4 o;
-    o.x = e4m3_to_bf16_bits(q[0] & 0xFF) | (e4m3_to_bf16_bits((q[0] >> 8) & 0xFF) << 16);
-    o.y = e4m3_to_bf16_bits((q[0] >> 16) & 0xFF) | (e4m3_to_bf16_bits(q[0] >> 24) << 16);
-    o.z = e4m3_to_bf16_bits(q[1] & 0xFF) | (e4m3_to_bf16_bits((q[1] >> 8) & 0xFF) << 16);
-    o.w = e4m3_to_bf16_bits((q[1] >> 16) & 0xFF) | (e4m3_to_bf16_bits(q[1] >> 24) << 16);
-    return o;
-  }
 }
 
 // Where a workgroup's tile lies: expert segment, rows, weight tile, K range.
@@ -387,22 +349,6 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-// 16 MFMAs of one 16-deep K slice.  GATEUP computes the transposed product
-// (weights as the A operand) so lanes hold consecutive hidden columns.
-template <int MODE>
-__device__ __forceinline__ void mfma_slice(f32x16 (&acc)[4][4], const bf16x8 (&af)[4],
-                                           const bf16x8 (&bfr)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (MODE == MODE_GATEUP)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // LDS-DMA kernel for bf16 weights: 256 x 256 tiles (2 x 2 waves of 128 x 128),
 // operands moved global -> LDS by buffer_load ... lds (no register staging,
@@ -456,13 +402,30 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 q) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 8 symmetric int8 codes (K order, low byte first) -> 8 bf16, exactly: each
+// code (|q| <= 127) has at most 7 significant bits.  Sign-extending byte
+// conversions to fp32, then pairs packed to bf16.
+__device__ __forceinline__ bf16x8 int8x8_to_bf16x8(uint2 q) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(float)(int8_t)(q.x >> (8 * i));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[4 + i] = (__bf16)(float)(int8_t)(q.y >> (8 * i));
+  return r;
+}
+
+// Weight formats of the GEMM: bf16, or 8-bit codes with fp32 scales per 128
+// output rows (OCP fp8 e4m3, or symmetric int8).
+enum { WQ_BF16 = 0, WQ_FP8 = 1, WQ_INT8 = 2 };
+
 // s_waitcnt with only the LDS counter constrained: lgkmcnt(0).
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX, bool FP8>
+template <int MODE, int KB, int NS, int MOE_AUX, int WQ>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  constexpr bool FP8 = WQ != WQ_BF16;  // 8-bit weight codes (fp8 or int8) with scales
   using C = DmaCfg<KB, NS, FP8>;
   constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
   constexpr int BNB = 256;
@@ -516,13 +479,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     }
   });
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
-  // With krot, workgroup tiles start their K walk at different points, so
-  // concurrent workgroups do not all read the same K slice (row strides are
-  // K*2 bytes, a power of two in the common shapes).
-  const int krot = p.krot ? __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)max(nk, 1))) : 0;
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    int kr = kt + krot;
-    kr = kr >= nk ? kr - nk : kr;
+  auto issue = [&](int kr, int stage) __attribute__((always_inline)) {
     char* gbase = dlds + stage * C::STAGE_BYTES +
                   (a_wave ? (wave & 1) * (C::TILE_BYTES / 2)
                           : C::TILE_BYTES + (wave & 1) * (C::B_TILE_BYTES / 2));
@@ -656,7 +613,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const bf16x8 bv = fp8x8_to_bf16x8(fb[kk][j]);
+              const bf16x8 bv = WQ == WQ_INT8 ? int8x8_to_bf16x8(fb[kk][j])
+                                              : fp8x8_to_bf16x8(fb[kk][j]);
 #pragma unroll
               for (int i = 0; i < NG; ++i) {
                 if (MODE == MODE_GATEUP)
@@ -886,11 +844,11 @@ inline unsigned sched_grid(const GemmParams& p) {
 // (one step in flight while one is computed: fewer barriers per K), and, for
 // tiles with few rows, 32-deep steps in three stages (two steps in flight:
 // such tiles have little compute to hide the operand latency behind).
-template <int MODE, bool FP8, int KB, int NS>
+template <int MODE, int WQ, int KB, int NS>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  using C = DmaCfg<KB, NS, FP8>;
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8>;
+  using C = DmaCfg<KB, NS, WQ != WQ_BF16>;
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ>;
   static int slots = 0;
   if (!slots) {
     hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -903,12 +861,25 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   p.slots = slots;
   constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
   if (slab_mode && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
-  grouped_gemm_dma_kernel<MODE, KB, NS, 1, FP8><<<sched_grid(p), 256, C::LDS, st>>>(p);
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ><<<sched_grid(p), 256, C::LDS, st>>>(p);
   if (slab_mode && p.split_max > 1)
     tail_fixup_kernel<MODE><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
+
+// Runtime weight format and pipeline shape -> the kernel instantiation.
+template <int MODE>
+hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
+  if (deep) {
+    if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 32, 3>(p, st);
+    if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 32, 3>(p, st);
+    return launch_gemm_dma<MODE, WQ_BF16, 32, 3>(p, st);
+  }
+  if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
+  if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
+  return launch_gemm_dma<MODE, WQ_BF16, 64, 2>(p, st);
+}
 
 }  // namespace
 
@@ -932,7 +903,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
     if (err == hipSuccess && ev_mid) err = hipEventRecord(ev_mid, st);
     return err;
   }
-  const bool fp8 = s.w_dtype == MOE_DT_FP8_E4M3;
+  const int wq = s.w_dtype == MOE_DT_FP8_E4M3 ? WQ_FP8 : (s.w_dtype == MOE_DT_INT8 ? WQ_INT8 : WQ_BF16);
   const int has_sh = s.has_shared ? 1 : 0;
   float* tail_slab = H ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
   const int tail_cap = L.tail_cap;
@@ -951,14 +922,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.mt_max = (int)mt_bound;
   g.tail_slab = tail_slab;
   g.tail_cap = tail_cap;
-  {
-    const char* kr = getenv("MOE_GEMM_KROT");
-    const char* ax = getenv("MOE_GEMM_AUX");
-    g.krot = kr ? atoi(kr) : 0;
-    g.cache_aux = ax ? atoi(ax) : 1;
-    const char* gr = getenv("MOE_GEMM_GROUP");  // weight tiles per block (tuning)
-    g.group_n = gr && atoi(gr) > 0 ? atoi(gr) : 8;
-  }
+  g.group_n = 8;  // weight tiles per expert-aligned block of the tile order
 
   // gate / up
   g.A = (const uint16_t*)x;
@@ -976,10 +940,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // few rows per expert (decode-sized batches): the deeper pipeline (measured
   // 6% faster at 16 rows per expert, slower at 128 and more)
   const bool deep = L.P_max / s.E <= 32;
-  hipError_t err = deep ? (fp8 ? launch_gemm_dma<MODE_GATEUP, true, 32, 3>(g, st)
-                               : launch_gemm_dma<MODE_GATEUP, false, 32, 3>(g, st))
-                        : (fp8 ? launch_gemm_dma<MODE_GATEUP, true, 64, 2>(g, st)
-                               : launch_gemm_dma<MODE_GATEUP, false, 64, 2>(g, st));
+  hipError_t err = launch_gemm<MODE_GATEUP>(wq, deep, g, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {
     err = hipEventRecord(ev_mid, st);
@@ -1010,14 +971,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.tail_slab = tail_slab;
   g2.tail_cap = tail_cap;
   if (y)
-    return deep ? (fp8 ? launch_gemm_dma<MODE_DOWN, true, 32, 3>(g2, st)
-                       : launch_gemm_dma<MODE_DOWN, false, 32, 3>(g2, st))
-                : (fp8 ? launch_gemm_dma<MODE_DOWN, true, 64, 2>(g2, st)
-                       : launch_gemm_dma<MODE_DOWN, false, 64, 2>(g2, st));
-  return deep ? (fp8 ? launch_gemm_dma<MODE_DOWN_PERM, true, 32, 3>(g2, st)
-                     : launch_gemm_dma<MODE_DOWN_PERM, false, 32, 3>(g2, st))
-              : (fp8 ? launch_gemm_dma<MODE_DOWN_PERM, true, 64, 2>(g2, st)
-                     : launch_gemm_dma<MODE_DOWN_PERM, false, 64, 2>(g2, st));
+    return launch_gemm<MODE_DOWN>(wq, deep, g2, st);
+  return launch_gemm<MODE_DOWN_PERM>(wq, deep, g2, st);
 }
 
 hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm,

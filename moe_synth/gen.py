@@ -24,7 +24,9 @@ are numpy uint16 bit patterns.
 
 The fp8 workload quantises the bf16 weights to OCP FP8 E4M3 with one fp32
 scale per group of 128 output features: s = amax(group)/448 and
-code = RNE(w/s), via torch's float8_e4m3fn conversion.  This is weight
+code = RNE(w/s), via torch's float8_e4m3fn conversion.  The int8 workload
+uses symmetric int8 codes with the same grouping: s = amax(group)/127 and
+code = RNE(w/s) in float32, clipped to [-127, 127].  This is weight
 preparation of the input, not part of the layer.
 """
 from __future__ import annotations
@@ -38,6 +40,7 @@ from .configs import CONFIGS, MoEConfig
 
 FP8_GROUP = 128
 FP8_MAX = 448.0
+INT8_MAX = 127.0
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -71,6 +74,18 @@ def _quant_fp8_rows(w_bf16: np.ndarray):
     q = (g / s[:, None, None]).clamp(-FP8_MAX, FP8_MAX)
     codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(out, inn)
     return codes.numpy().copy(), s.numpy().copy()
+
+
+def _quant_int8_rows(w_bf16: np.ndarray):
+    """Quantise a [out, in] bf16 matrix to symmetric int8 codes with
+    per-128-row scales."""
+    w = bf16_bits_to_f32(w_bf16)
+    out, inn = w.shape
+    g = w.reshape(out // FP8_GROUP, FP8_GROUP, inn)
+    amax = np.maximum(np.abs(g).max(axis=(1, 2)), np.float32(1e-30))
+    s = (amax / np.float32(INT8_MAX)).astype(np.float32)
+    q = np.clip(np.rint(g / s[:, None, None]), -INT8_MAX, INT8_MAX).astype(np.int8)
+    return q.reshape(out, inn), s
 
 
 class Workload:
@@ -138,6 +153,11 @@ class Workload:
             q1, s1 = _quant_fp8_rows(W1)
             q3, s3 = _quant_fp8_rows(W3)
             q2, s2 = _quant_fp8_rows(W2)
+            return {"W1": q1, "W3": q3, "W2": q2, "s1": s1, "s3": s3, "s2": s2}
+        if self.cfg.w == "int8":
+            q1, s1 = _quant_int8_rows(W1)
+            q3, s3 = _quant_int8_rows(W3)
+            q2, s2 = _quant_int8_rows(W2)
             return {"W1": q1, "W3": q3, "W2": q2, "s1": s1, "s3": s3, "s2": s2}
         return {"W1": W1, "W3": W3, "W2": W2}
 

@@ -32,6 +32,7 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
                        cases in tests/golden, the D'Hondt highest-quotient
                        statement of the replication, placement invariants)
   fp8 e4m3 decode      pinned (OCP format values, torch float8_e4m3fn)
+  int8 dequantisation  pinned (code * scale per 128 rows, against torch's int8 cast)
   full-size workloads  parity unpinned beyond the invariants above (the pages
                        print no outputs for those shapes)
 """
@@ -43,3 +44,4 @@ from .moe_oracle import (  # noqa: F401
 from .stats import (expert_imbalance, lpt_pack, naive_split, sample_variance,  # noqa: F401
                     replicate, replica_loads, eplb_plan)
 from .fp8 import e4m3_decode_table, dequant_rows  # noqa: F401
+from .int8 import dequant_int8_rows  # noqa: F401

@@ -34,8 +34,9 @@ give it:
                                                 shared experts)
 
 Inputs: x as float32 or bfloat16 bit patterns (uint16); W_g float32 [d, E];
-expert weights output-major ([out, in]) as float32, bf16 bits, or fp8 e4m3
-codes (uint8) with float32 scales per 128 output features.
+expert weights output-major ([out, in]) as float32, bf16 bits, fp8 e4m3
+codes (uint8) or symmetric int8 codes (int8), the codes with float32 scales
+per 128 output features.
 """
 from __future__ import annotations
 
@@ -44,6 +45,7 @@ import math
 import numpy as np
 
 from .fp8 import dequant_rows
+from .int8 import dequant_int8_rows
 
 
 # ---------------------------------------------------------------- numerics
@@ -56,10 +58,13 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 
 def _weight(w: dict, name: str) -> np.ndarray:
-    """One expert matrix in float64; fp8 codes are decoded and scaled exactly."""
+    """One expert matrix in float64; fp8 (uint8) or int8 codes are decoded and
+    scaled exactly."""
     a = w[name]
     if a.dtype == np.uint8:
         return dequant_rows(a, w["s" + name[1:]])
+    if a.dtype == np.int8:
+        return dequant_int8_rows(a, w["s" + name[1:]])
     return widen(a)
 
 

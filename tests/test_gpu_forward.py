@@ -50,6 +50,12 @@ SMALL = [
     # its gate and up partial sums finished (SwiGLU) by the fixup pass
     (300, 4096, 4, 2, 256, None, True, "bf16", None),
     (300, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
+    # int8 weights: full tiles, few rows per expert (three-stage pipeline),
+    # a shared expert, a capacity limit
+    (1100, 512, 8, 2, 384, None, True, "int8", None),
+    (64, 512, 8, 2, 1408, None, False, "int8", None),
+    (96, 256, 16, 2, 384, 0.75, True, "int8", "zipf1.5"),
+    (600, 512, 4, 2, 4096, None, False, "int8", None),
 ]
 
 
@@ -169,7 +175,7 @@ def _sample_tokens(T, n, seed):
 
 @pytest.mark.parametrize("name,nsample", [("mixtral", 40), ("decode", 64),
                                           ("capacity_skew", 40), ("fine_grained", 12),
-                                          ("fine_grained_fp8", 12)])
+                                          ("fine_grained_fp8", 12), ("fine_grained_int8", 12)])
 def test_workload_full_size(moe, name, nsample):
     print(f"[workload] {name}", flush=True)
     wl = Workload(get_config(name))

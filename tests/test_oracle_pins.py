@@ -664,3 +664,27 @@ def test_dequant_rows_group_scaling():
     s = np.array([0.5, 4.0], np.float32)
     W = oracle.dequant_rows(codes, s)
     assert np.all(W[:128] == 0.5) and np.all(W[128:] == 4.0)
+
+
+def test_int8_dequant_definition_and_torch():
+    """weight = code * scale, one scale per 128 output rows; the codes are the
+    two's-complement bytes (torch's int8 cast agrees), and the synthetic
+    quantiser keeps |code| <= 127 with round-trip error <= scale / 2."""
+    codes = np.array([[-127, -1, 0, 1, 127]] * 256, dtype=np.int8)
+    s = np.array([0.25, 3.0], np.float32)
+    W = oracle.dequant_int8_rows(codes, s)
+    assert W[0].tolist() == [-31.75, -0.25, 0.0, 0.25, 31.75]
+    assert W[200].tolist() == [-381.0, -3.0, 0.0, 3.0, 381.0]
+    import torch
+    allc = np.arange(-128, 128, dtype=np.int64).astype(np.int8).reshape(1, 256).repeat(128, 0)
+    ref = torch.from_numpy(allc).to(torch.float64).numpy() * 0.5
+    assert np.array_equal(oracle.dequant_int8_rows(allc, np.array([0.5], np.float32)), ref)
+    from moe_synth.gen import _quant_int8_rows, f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(3)
+    w = f32_to_bf16_bits(rng.standard_normal((256, 64)).astype(np.float32))
+    q, sc = _quant_int8_rows(w)
+    assert q.dtype == np.int8 and np.abs(q.astype(np.int32)).max() == 127
+    back = oracle.dequant_int8_rows(q, sc)
+    err = np.abs(back - bf16_bits_to_f32(w).astype(np.float64))
+    assert np.all(err <= np.repeat(sc.astype(np.float64), 128)[:, None] / 2 * (1 + 1e-6))
+

@@ -50,6 +50,9 @@ SMALL = [
     # its gate and up partial sums finished (SwiGLU) by the fixup pass
     (300, 4096, 4, 2, 256, None, True, "bf16", None),
     (300, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
+    # degenerate routing: one expert (k = E = 1), every expert (k = E = 4)
+    (200, 256, 1, 1, 256, None, False, "bf16", None),
+    (150, 256, 4, 4, 128, 1.0, True, "bf16", None),
     # int8 weights: full tiles, few rows per expert (three-stage pipeline),
     # a shared expert, a capacity limit
     (1100, 512, 8, 2, 384, None, True, "int8", None),

@@ -418,6 +418,15 @@ __device__ __forceinline__ bf16x8 int8x8_to_bf16x8(uint2 q) {
 // output rows (OCP fp8 e4m3, or symmetric int8).
 enum { WQ_BF16 = 0, WQ_FP8 = 1, WQ_INT8 = 2 };
 
+// wait_vmcnt for a count known only at run time (wave-uniform, 0..NMAX):
+// s_waitcnt takes an immediate, so one branch per possible count.
+template <int NMAX>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  static_for<NMAX + 1>([&](auto c) {
+    if (n == decltype(c)::value) wait_vmcnt<decltype(c)::value>();
+  });
+}
+
 // s_waitcnt with only the LDS counter constrained: lgkmcnt(0).
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
@@ -479,6 +488,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     }
   });
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
+  // Activation DMA instructions whose rows all lie past the segment's end
+  // are not issued at all.  A wave's rows are contiguous, so its valid
+  // instructions are a prefix, a_valid of them at every step; the waits for
+  // "k steps still in flight" count them.
+  const int a_valid = [&] {
+    if (!a_wave) return C::NI;
+    const int left = t.rows - t.m0 - (wave & 1) * C::NI * C::ROWS_PER_INST;
+    return __builtin_amdgcn_readfirstlane(
+        max(0, min(C::NI, (left + C::ROWS_PER_INST - 1) / C::ROWS_PER_INST)));
+  }();
   auto issue = [&](int kr, int stage) __attribute__((always_inline)) {
     char* gbase = dlds + stage * C::STAGE_BYTES +
                   (a_wave ? (wave & 1) * (C::TILE_BYTES / 2)
@@ -486,11 +505,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     const int soff = __builtin_amdgcn_readfirstlane(kr * (a_wave ? C::RB : C::RBB));
     if constexpr (C::NI == C::NIB) {
       static_for<C::NI>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+        if (j < a_valid)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
     } else if (a_wave) {
       static_for<C::NI>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+        if (j < a_valid)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
     } else {
       static_for<C::NIB>([&](auto j) {
@@ -545,8 +566,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // different count per wave kind
   auto wait_steps = [&](auto KS) __attribute__((always_inline)) {
     constexpr int k = decltype(KS)::value;
-    if (a_wave)
-      wait_vmcnt<k * C::NI>();
+    if constexpr (k == 0)
+      wait_vmcnt<0>();
+    else if (a_wave)
+      wait_vmcnt_dyn<k * C::NI>(k * a_valid);
     else
       wait_vmcnt<k * C::NIB>();
   };

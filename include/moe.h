@@ -100,7 +100,8 @@ typedef enum moe_overflow {
 typedef struct moe_shape {
   int64_t T;          /* tokens, >= 0 */
   int32_t d;          /* model width */
-  int32_t E;          /* routed experts, 1..1024 */
+  int32_t E;          /* routed experts, 1..1024 (moe_route / moe_forward: up to 256
+                         with fp32 x, 1024 with bf16 x) */
   int32_t top_k;      /* experts per token, 1..min(E, 32) */
   int32_t d_ff;       /* expert hidden width (ignored for LINEAR_BIAS) */
   int32_t capacity;   /* tokens per expert, -1 = unlimited (see moe_capacity) */

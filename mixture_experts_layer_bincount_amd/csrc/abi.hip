@@ -307,7 +307,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* W_g, co
                      float* logits, int32_t* topk_idx, float* topk_w, void* ws, void* stream) {
   MOE_TRY(check_shape(shape, false));
   const moe_shape& s = *shape;
-  if (s.E > 256) return fail(MOE_ERR_UNSUPPORTED, "moe_route supports E <= 256 (E=%d)", s.E);
+  if (s.E > 256 && !router_mfma_epad(s))
+    return fail(MOE_ERR_UNSUPPORTED, "more than 256 experts need bf16 x with d %% 32 == 0 (E=%d)", s.E);
   if (s.T == 0) return MOE_OK;
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(W_g, "W_g"));
@@ -440,7 +441,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
                        int32_t* counts, int32_t* offsets, void* ws, void* stream) {
   MOE_TRY(check_shape(shape, true));
   const moe_shape& s = *shape;
-  if (s.E > 256) return fail(MOE_ERR_UNSUPPORTED, "moe_forward supports E <= 256 (E=%d)", s.E);
+  if (s.E > 256 && !router_mfma_epad(s))
+    return fail(MOE_ERR_UNSUPPORTED, "more than 256 experts need bf16 x with d %% 32 == 0 (E=%d)", s.E);
   MOE_TRY(check_ptr(counts, "counts"));
   MOE_TRY(check_ptr(offsets, "offsets"));
   MOE_TRY(check_ptr(ws, "ws", 256));

@@ -81,6 +81,9 @@ bool use_grouped_combine(const moe_shape& s);
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All are asynchronous.
 int router_splits_for(const moe_shape& s);
+// Experts padded to the MFMA router's 16-multiple (power of two), or 0 when
+// the fp32-activation router runs instead (it handles up to 256 experts).
+int router_mfma_epad(const moe_shape& s);
 size_t router_split_bytes(const moe_shape& s);
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
                               float* partial, int splits, void* split_ws, hipStream_t st);

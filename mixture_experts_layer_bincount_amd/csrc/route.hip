@@ -347,7 +347,7 @@ hipError_t router_gemm_dispatch(const moe_shape& s, const XT* x, const float* W_
 }  // namespace
 
 int router_mfma_epad(const moe_shape& s) {
-  if (s.act_dtype != MOE_DT_BF16 || s.d % 32 != 0 || s.E > 256) return 0;
+  if (s.act_dtype != MOE_DT_BF16 || s.d % 32 != 0 || s.E > 1024) return 0;
   int e = 16;
   while (e < s.E) e *= 2;
   return e;
@@ -392,7 +392,8 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_
                                                 ep, per);                                         \
     return hipGetLastError();                                                                     \
   }
-    MOE_RL(16, 1) MOE_RL(32, 2) MOE_RL(64, 4) MOE_RL(128, 4) MOE_RL(256, 4)
+    MOE_RL(16, 1) MOE_RL(32, 2) MOE_RL(64, 4) MOE_RL(128, 4) MOE_RL(256, 4) MOE_RL(512, 4)
+    MOE_RL(1024, 4)
 #undef MOE_RL
     return hipErrorInvalidValue;
   }

@@ -50,6 +50,10 @@ SMALL = [
     # its gate and up partial sums finished (SwiGLU) by the fixup pass
     (300, 4096, 4, 2, 256, None, True, "bf16", None),
     (300, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
+    # the largest expert counts: 512 and 1024 experts (16 expert blocks in
+    # the router, 1024 segments in the GEMM schedule)
+    (700, 256, 512, 4, 128, None, False, "bf16", None),
+    (1500, 256, 1024, 8, 128, 1.0, True, "bf16", None),
     # degenerate routing: one expert (k = E = 1), every expert (k = E = 4)
     (200, 256, 1, 1, 256, None, False, "bf16", None),
     (150, 256, 4, 4, 128, 1.0, True, "bf16", None),

@@ -60,9 +60,10 @@ def test_route_from_logits_bit_exact(moe, T, E, k, ties):
     (64, 8, 4, 2, "f32", False), (1000, 512, 64, 2, "bf16", True),
     (300, 1024, 256, 8, "bf16", False), (64, 4096, 8, 2, "bf16", False),
     (517, 256, 8, 2, "bf16", True), (1, 256, 16, 4, "bf16", False),
-    # 32 and 128 experts (2 and 4 waves along the experts); d = 4160 leaves
-    # the last K split of the MFMA router empty
-    (700, 320, 32, 2, "bf16", True), (2000, 4160, 128, 4, "bf16", False)])
+    # 32 and 128 experts; d = 4160 leaves the last K split of the MFMA router
+    # empty; 512 and 1024 experts (8 and 16 expert blocks)
+    (700, 320, 32, 2, "bf16", True), (2000, 4160, 128, 4, "bf16", False),
+    (300, 512, 512, 8, "bf16", True), (100, 256, 1024, 32, "bf16", False)])
 def test_route_fused(moe, T, d, E, k, act, bias):
     print(f"[route] T={T} d={d} E={E} k={k} act={act}", flush=True)
     kind = "linear_bias" if act == "f32" else "swiglu"

@@ -24,11 +24,13 @@
 // rows of W3, so the SwiGLU happens in registers; the product is computed
 // transposed (weights as the MFMA A operand) so each lane holds 4
 // consecutive hidden columns of one row and stores them as one 8-byte write.
-// Operands move global -> LDS by buffer_load ... lds (two 64-deep stages,
-// XOR-swizzled rows, no bank conflicts on the 16-byte fragment reads); the
-// next 32-deep slice's fragments are read under the current slice's MFMAs;
-// one barrier per step.  fp8 (e4m3) weights land in LDS as bytes and are
-// widened exactly to bf16 in registers; their scales apply in the epilogue.
+// Operands move global -> LDS by buffer_load ... lds (two 64-deep stages, or
+// three 32-deep ones for decode-sized batches; XOR-swizzled rows, no bank
+// conflicts on the 16-byte fragment reads; no loads for activation rows past
+// the segment's end); the next 32-deep slice's fragments are read under the
+// current slice's MFMAs; one barrier per step.  8-bit weights (OCP fp8 e4m3
+// or symmetric int8) land in LDS as bytes and are widened exactly to bf16 in
+// registers; their per-128-row scales apply in the epilogue.
 // Tile order (tile_sched.h): the real tiles, counted on the device, are dealt
 // evenly to the XCDs in expert-aligned blocks, so the workgroups one XCD runs
 // at the same time share operands in its L2.  The tiles of the last, partial

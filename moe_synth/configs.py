@@ -26,7 +26,7 @@ class MoEConfig:
     d_ff: int         # expert hidden width (0 for the Linear+bias expert)
     kind: str         # "linear_bias" | "swiglu"
     act: str          # activation / x dtype: "f32" | "bf16"
-    w: str            # expert weight dtype: "f32" | "bf16" | "fp8_e4m3" | "int8"
+    w: str            # expert weight dtype: "f32" | "bf16" | "fp8_e4m3" | "int8" | "int4"
     cf: Optional[float] = None       # capacity factor; None = unlimited
     router_bias: Optional[str] = None  # None | "zipf1.5": b_e = 1.5*ln(1/(e+1))
     shared: bool = False             # one always-on shared expert
@@ -60,6 +60,9 @@ CONFIGS = {
     "fine_grained_int8": MoEConfig("fine_grained_int8", T=4096, d=7168, E=256,
                                    k=8, d_ff=2048, kind="swiglu", act="bf16",
                                    w="int8", shared=True, seed=SEED_BASE + 4),
+    "fine_grained_int4": MoEConfig("fine_grained_int4", T=4096, d=7168, E=256,
+                                   k=8, d_ff=2048, kind="swiglu", act="bf16",
+                                   w="int4", shared=True, seed=SEED_BASE + 4),
     "capacity_skew": MoEConfig("capacity_skew", T=16384, d=4096, E=64, k=2,
                                d_ff=1408, kind="swiglu", act="bf16", w="bf16",
                                cf=1.25, router_bias="zipf1.5",

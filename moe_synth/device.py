@@ -8,7 +8,10 @@ from .gen import Workload
 
 
 def to_device(a: np.ndarray, device) -> torch.Tensor:
-    """numpy -> torch on `device`; uint16 arrays become bfloat16 tensors."""
+    """numpy -> torch on `device`; uint16 arrays become bfloat16 tensors,
+    packed int4 (one-field structured bytes) uint8 tensors."""
+    if a.dtype.names:
+        a = np.ascontiguousarray(a).view(np.uint8)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
     if a.dtype == np.uint8:

@@ -26,8 +26,11 @@ The fp8 workload quantises the bf16 weights to OCP FP8 E4M3 with one fp32
 scale per group of 128 output features: s = amax(group)/448 and
 code = RNE(w/s), via torch's float8_e4m3fn conversion.  The int8 workload
 uses symmetric int8 codes with the same grouping: s = amax(group)/127 and
-code = RNE(w/s) in float32, clipped to [-127, 127].  This is weight
-preparation of the input, not part of the layer.
+code = RNE(w/s) in float32, clipped to [-127, 127].  The int4 workload does
+the same with s = amax(group)/7 and codes clipped to [-7, 7], packed two per
+byte along the input dimension (even index in the low nibble) into the
+one-field structured dtype INT4X2.  This is weight preparation of the input,
+not part of the layer.
 """
 from __future__ import annotations
 
@@ -41,6 +44,10 @@ from .configs import CONFIGS, MoEConfig
 FP8_GROUP = 128
 FP8_MAX = 448.0
 INT8_MAX = 127.0
+INT4_MAX = 7.0
+# packed int4 codes: a one-field structured byte, so they are told apart from
+# int8 or fp8 codes by their dtype
+INT4X2 = np.dtype([("int4x2", np.uint8)])
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -86,6 +93,20 @@ def _quant_int8_rows(w_bf16: np.ndarray):
     s = (amax / np.float32(INT8_MAX)).astype(np.float32)
     q = np.clip(np.rint(g / s[:, None, None]), -INT8_MAX, INT8_MAX).astype(np.int8)
     return q.reshape(out, inn), s
+
+
+def _quant_int4_rows(w_bf16: np.ndarray):
+    """Quantise a [out, in] bf16 matrix to symmetric int4 codes with
+    per-128-row scales, packed two per byte ([out, in/2], INT4X2)."""
+    w = bf16_bits_to_f32(w_bf16)
+    out, inn = w.shape
+    g = w.reshape(out // FP8_GROUP, FP8_GROUP, inn)
+    amax = np.maximum(np.abs(g).max(axis=(1, 2)), np.float32(1e-30))
+    s = (amax / np.float32(INT4_MAX)).astype(np.float32)
+    q = np.clip(np.rint(g / s[:, None, None]), -INT4_MAX, INT4_MAX).astype(np.int8)
+    u = q.reshape(out, inn).view(np.uint8) & np.uint8(0xF)
+    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return np.ascontiguousarray(packed).view(INT4X2), s
 
 
 class Workload:
@@ -154,10 +175,11 @@ class Workload:
             q3, s3 = _quant_fp8_rows(W3)
             q2, s2 = _quant_fp8_rows(W2)
             return {"W1": q1, "W3": q3, "W2": q2, "s1": s1, "s3": s3, "s2": s2}
-        if self.cfg.w == "int8":
-            q1, s1 = _quant_int8_rows(W1)
-            q3, s3 = _quant_int8_rows(W3)
-            q2, s2 = _quant_int8_rows(W2)
+        if self.cfg.w in ("int8", "int4"):
+            quant = _quant_int8_rows if self.cfg.w == "int8" else _quant_int4_rows
+            q1, s1 = quant(W1)
+            q3, s3 = quant(W3)
+            q2, s2 = quant(W2)
             return {"W1": q1, "W3": q3, "W2": q2, "s1": s1, "s3": s3, "s2": s2}
         return {"W1": W1, "W3": W3, "W2": W2}
 

@@ -33,6 +33,8 @@ Parity status per function (how each is pinned is in tests/test_oracle_pins.py):
                        statement of the replication, placement invariants)
   fp8 e4m3 decode      pinned (OCP format values, torch float8_e4m3fn)
   int8 dequantisation  pinned (code * scale per 128 rows, against torch's int8 cast)
+  int4 dequantisation  pinned (hand-worked packed bytes, numpy's arithmetic shifts of
+                       the byte for all 256 values, reduction to the int8 case)
   full-size workloads  parity unpinned beyond the invariants above (the pages
                        print no outputs for those shapes)
 """
@@ -45,3 +47,4 @@ from .stats import (expert_imbalance, lpt_pack, naive_split, sample_variance,  #
                     replicate, replica_loads, eplb_plan)
 from .fp8 import e4m3_decode_table, dequant_rows  # noqa: F401
 from .int8 import dequant_int8_rows  # noqa: F401
+from .int4 import INT4X2, dequant_int4_rows, unpack_int4  # noqa: F401

@@ -35,8 +35,9 @@ give it:
 
 Inputs: x as float32 or bfloat16 bit patterns (uint16); W_g float32 [d, E];
 expert weights output-major ([out, in]) as float32, bf16 bits, fp8 e4m3
-codes (uint8) or symmetric int8 codes (int8), the codes with float32 scales
-per 128 output features.
+codes (uint8), symmetric int8 codes (int8) or packed symmetric int4 codes
+(the INT4X2 dtype, [out, in/2]), the codes with float32 scales per 128 output
+features.
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ import math
 import numpy as np
 
 from .fp8 import dequant_rows
+from .int4 import dequant_int4_rows, is_int4x2
 from .int8 import dequant_int8_rows
 
 
@@ -58,9 +60,11 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 
 def _weight(w: dict, name: str) -> np.ndarray:
-    """One expert matrix in float64; fp8 (uint8) or int8 codes are decoded and
-    scaled exactly."""
+    """One expert matrix in float64; fp8 (uint8), int8 or packed int4 codes are
+    decoded and scaled exactly."""
     a = w[name]
+    if is_int4x2(a):
+        return dequant_int4_rows(a, w["s" + name[1:]])
     if a.dtype == np.uint8:
         return dequant_rows(a, w["s" + name[1:]])
     if a.dtype == np.int8:

@@ -10,7 +10,7 @@ import oracle
 from moe_synth import Workload
 
 MARGIN_EXCLUDE = 1e-5            # tokens with a smaller top-k margin may flip
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_e4m3": 6e-2, "int8": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_e4m3": 6e-2, "int8": 2e-2, "int4": 2e-2}
 LOGIT_TOL = 1e-4                 # fp32 router logits against the float64 oracle
 
 

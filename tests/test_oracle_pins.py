@@ -688,3 +688,48 @@ def test_int8_dequant_definition_and_torch():
     err = np.abs(back - bf16_bits_to_f32(w).astype(np.float64))
     assert np.all(err <= np.repeat(sc.astype(np.float64), 128)[:, None] / 2 * (1 + 1e-6))
 
+
+
+def test_int4_dequant_hand_worked_bytes():
+    """Packed int4 (two codes per byte, even input index in the low nibble,
+    4-bit two's complement), worked by hand: 0x10 -> (0, 1), 0xF7 -> (7, -1),
+    0x8F -> (-1, -8), 0x00 -> (0, 0); rows 128.. take the second scale."""
+    b = np.array([[0x10, 0xF7, 0x8F, 0x00]] * 256, dtype=np.uint8).view(oracle.INT4X2)
+    W = oracle.dequant_int4_rows(b, np.array([0.5, 2.0], np.float32))
+    assert W.shape == (256, 8)
+    assert W[0].tolist() == [0.0, 0.5, 3.5, -0.5, -0.5, -4.0, 0.0, 0.0]
+    assert W[255].tolist() == [0.0, 2.0, 14.0, -2.0, -2.0, -16.0, 0.0, 0.0]
+
+
+def test_int4_unpack_all_bytes_by_arithmetic_shift():
+    """Every byte value: the low code is the byte shifted left by 4 then
+    arithmetically right by 4 as an int8, the high code the byte as an int8
+    shifted arithmetically right by 4 (numpy's sign-extending shifts)."""
+    allb = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    got = oracle.unpack_int4(allb.view(oracle.INT4X2))
+    lo = (allb << np.uint8(4)).view(np.int8) >> np.int8(4)
+    hi = allb.view(np.int8) >> np.int8(4)
+    assert np.array_equal(got[:, 0::2], lo.astype(np.int64))
+    assert np.array_equal(got[:, 1::2], hi.astype(np.int64))
+
+
+def test_int4_reduces_to_int8_and_synthetic_round_trip():
+    """Codes in [-7, 7] packed as int4 decode to the same weights as the
+    same codes stored as int8; the synthetic quantiser keeps |code| <= 7
+    (7 reached in every group) with round-trip error <= scale / 2."""
+    rng = np.random.default_rng(11)
+    codes = rng.integers(-7, 8, size=(256, 64)).astype(np.int8)
+    u = codes.view(np.uint8) & np.uint8(0xF)
+    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).view(oracle.INT4X2)
+    s = np.array([0.125, 3.0], np.float32)
+    assert np.array_equal(oracle.dequant_int4_rows(packed, s), oracle.dequant_int8_rows(codes, s))
+    from moe_synth.gen import _quant_int4_rows, f32_to_bf16_bits, bf16_bits_to_f32
+    w = f32_to_bf16_bits(rng.standard_normal((256, 64)).astype(np.float32))
+    q, sc = _quant_int4_rows(w)
+    assert q.shape == (256, 32)
+    c = oracle.unpack_int4(q)
+    assert np.abs(c).max() == 7
+    assert all(np.abs(c[g * 128:(g + 1) * 128]).max() == 7 for g in range(2))
+    back = oracle.dequant_int4_rows(q, sc)
+    err = np.abs(back - bf16_bits_to_f32(w).astype(np.float64))
+    assert np.all(err <= np.repeat(sc.astype(np.float64), 128)[:, None] / 2 * (1 + 1e-6))

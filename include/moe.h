@@ -40,8 +40,9 @@
  *   b_g      [E]           fp32 router bias, optional
  *   W1, W3   [E, d_ff, d]  expert gate / up projections, [out, in] per expert
  *   W2       [E, d, d_ff]  expert down projection, [out, in] per expert
- *   s1, s3   [E, d_ff/128] fp32 scales of fp8 or int8 W1 / W3 (one per 128 output rows)
- *   s2       [E, d/128]    fp32 scales of fp8 or int8 W2
+ *   s1, s3   [E, d_ff/128] fp32 scales of fp8, int8 or int4 W1 / W3 (one per 128 output rows)
+ *   s2       [E, d/128]    fp32 scales of fp8, int8 or int4 W2
+ *            (int4 matrices hold in/2 bytes per row: W1, W3 [E, d_ff, d/2], W2 [E, d, d_ff/2])
  *   W1s, W3s [d_ff, d], W2s [d, d_ff] (+ s1s, s3s [d_ff/128], s2s [d/128])
  *                          the shared expert (one always-on expert, weight 1)
  *   W        [E, d, d]     Linear+bias experts, [out, in];  b [E, d]
@@ -74,8 +75,12 @@ typedef enum moe_dtype {
   MOE_DT_F32 = 0,
   MOE_DT_BF16 = 1,
   MOE_DT_FP8_E4M3 = 2, /* OCP FP8 E4M3 (bias 7, max 448, no infinities) */
-  MOE_DT_INT8 = 3      /* symmetric int8 codes -127..127 (iopenshare §5.3: INT8 expert
+  MOE_DT_INT8 = 3,     /* symmetric int8 codes -127..127 (iopenshare §5.3: INT8 expert
                           weights); weight = code * scale */
+  MOE_DT_INT4 = 4      /* symmetric int4 codes -7..7 (iopenshare §5.3: INT4 expert weights),
+                          two per byte along the input dimension, the even input index
+                          in the low nibble; a nibble is two's complement (0x8 reads as
+                          -8); weight = code * scale */
 } moe_dtype;
 
 typedef enum moe_expert_kind {
@@ -106,7 +111,8 @@ typedef struct moe_shape {
   int32_t d_ff;       /* expert hidden width (ignored for LINEAR_BIAS) */
   int32_t capacity;   /* tokens per expert, -1 = unlimited (see moe_capacity) */
   int32_t act_dtype;  /* moe_dtype of x: BF16 for SWIGLU, F32 for LINEAR_BIAS */
-  int32_t w_dtype;    /* moe_dtype of expert weights: BF16, FP8_E4M3 or INT8 (SWIGLU), F32 (LINEAR_BIAS) */
+  int32_t w_dtype;    /* moe_dtype of expert weights: BF16, FP8_E4M3, INT8 or INT4 (SWIGLU),
+                         F32 (LINEAR_BIAS) */
   int32_t kind;       /* moe_expert_kind */
   int32_t has_shared; /* 1: add one always-on SWIGLU shared expert (weight 1) */
   int32_t overflow;   /* moe_overflow; 0 (drop) when zero-initialised */

@@ -22,7 +22,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-DT_F32, DT_BF16, DT_FP8_E4M3, DT_INT8 = 0, 1, 2, 3
+DT_F32, DT_BF16, DT_FP8_E4M3, DT_INT8, DT_INT4 = 0, 1, 2, 3, 4
 LINEAR_BIAS, SWIGLU = 0, 1
 OVERFLOW_DROP, OVERFLOW_REROUTE, OVERFLOW_SHARED = 0, 1, 2
 OVERFLOW = {"drop": OVERFLOW_DROP, "reroute": OVERFLOW_REROUTE, "shared": OVERFLOW_SHARED}

@@ -69,8 +69,9 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     return fail(MOE_ERR_INVALID, "T*top_k exceeds int32");
   if (s->kind == MOE_EXPERT_SWIGLU) {
     if (s->act_dtype != MOE_DT_BF16) return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts need bf16 x");
-    if (s->w_dtype != MOE_DT_BF16 && s->w_dtype != MOE_DT_FP8_E4M3 && s->w_dtype != MOE_DT_INT8)
-      return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts need bf16, fp8-e4m3 or int8 weights");
+    if (s->w_dtype != MOE_DT_BF16 && s->w_dtype != MOE_DT_FP8_E4M3 && s->w_dtype != MOE_DT_INT8 &&
+        s->w_dtype != MOE_DT_INT4)
+      return fail(MOE_ERR_UNSUPPORTED, "SwiGLU experts need bf16, fp8-e4m3, int8 or int4 weights");
     if (need_ffn) {
       if (s->d % 64 != 0) return fail(MOE_ERR_INVALID, "d=%d must be a multiple of 64", s->d);
       if (s->d_ff <= 0 || s->d_ff % 128 != 0)
@@ -114,7 +115,7 @@ moe_status check_weights(const moe_shape* s, const moe_weights* w) {
     MOE_TRY(check_ptr(w->b, "b"));
     return MOE_OK;
   }
-  const bool fp8 = s->w_dtype == MOE_DT_FP8_E4M3 || s->w_dtype == MOE_DT_INT8;  // 8-bit + scales
+  const bool fp8 = s->w_dtype != MOE_DT_BF16;  // quantised codes (8 or 4 bits) + scales
   const size_t al = fp8 ? 8 : 16;
   MOE_TRY(check_ptr(w->W1, "W1", al));
   MOE_TRY(check_ptr(w->W3, "W3", al));

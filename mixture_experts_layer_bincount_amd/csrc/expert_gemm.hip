@@ -362,7 +362,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 constexpr int DMA_BM = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int KB, int NS, bool FP8>
+template <int KB, int NS, int WBITS>
 struct DmaCfg {
   // activation (A) tile: 256 rows of KB bf16
   static constexpr int RB = KB * 2;                 // bytes per A row and stage
@@ -371,8 +371,8 @@ struct DmaCfg {
   static constexpr int ROWS_PER_INST = 1024 / RB;   // A rows one wave-level DMA fills
   static constexpr int NI = 128 / ROWS_PER_INST;    // A DMA instructions per wave and stage
   static constexpr int TILE_BYTES = 256 * RB;       // the A tile
-  // weight (B) tile: 256 rows of KB bf16, or KB fp8 codes
-  static constexpr int RBB = KB * (FP8 ? 1 : 2);    // bytes per B row and stage
+  // weight (B) tile: 256 rows of KB weights of WBITS bits (16 bf16, 8 or 4)
+  static constexpr int RBB = KB * WBITS / 8;         // bytes per B row and stage
   static constexpr int CPRB = RBB / 16;
   static constexpr int RPSB = 256 / RBB;
   static constexpr int ROWS_PER_INST_B = 1024 / RBB;
@@ -381,7 +381,7 @@ struct DmaCfg {
   static constexpr int STAGE_BYTES = TILE_BYTES + B_TILE_BYTES;
   static constexpr int NI_MAX = NI > NIB ? NI : NIB;
   static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
-  static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4, "DMA pipeline shape");
+  static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4 && RBB >= 16, "DMA pipeline shape");
   static_assert(LDS <= 150 * 1024, "LDS budget (with the static tile-map arrays)");
 };
 
@@ -416,9 +416,19 @@ __device__ __forceinline__ bf16x8 int8x8_to_bf16x8(uint2 q) {
   return r;
 }
 
-// Weight formats of the GEMM: bf16, or 8-bit codes with fp32 scales per 128
-// output rows (OCP fp8 e4m3, or symmetric int8).
-enum { WQ_BF16 = 0, WQ_FP8 = 1, WQ_INT8 = 2 };
+// 8 symmetric int4 codes (K order, low nibble first) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 int4x8_to_bf16x8(uint32_t q) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)((int32_t)(q << (28 - 4 * i)) >> 28);
+  return r;
+}
+
+// Weight formats of the GEMM: bf16, or 8-bit / 4-bit codes with fp32 scales
+// per 128 output rows (OCP fp8 e4m3, symmetric int8, symmetric int4 packed
+// two per byte, low nibble first).
+enum { WQ_BF16 = 0, WQ_FP8 = 1, WQ_INT8 = 2, WQ_INT4 = 3 };
+constexpr int wq_bits(int wq) { return wq == WQ_BF16 ? 16 : (wq == WQ_INT4 ? 4 : 8); }
 
 // wait_vmcnt for a count known only at run time (wave-uniform, 0..NMAX):
 // s_waitcnt takes an immediate, so one branch per possible count.
@@ -436,9 +446,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 template <int MODE, int KB, int NS, int MOE_AUX, int WQ>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  constexpr bool FP8 = WQ != WQ_BF16;  // 8-bit weight codes (fp8 or int8) with scales
-  using C = DmaCfg<KB, NS, FP8>;
-  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight element
+  constexpr bool FP8 = WQ != WQ_BF16;  // quantised weight codes with scales
+  constexpr int WBITS = wq_bits(WQ);
+  using C = DmaCfg<KB, NS, WBITS>;
   constexpr int BNB = 256;
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
   TileMap t;
@@ -457,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // lane / CPR (B: the _B / CPRB / NIB counterparts); lane i writes chunk slot
   // i % CPR, which holds K chunk (i % CPR) ^ swz(row).
   const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
-  const int64_t ebytes = (int64_t)N * K * WB;
+  const int64_t ebytes = (int64_t)N * K * WBITS / 8;
   const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
   // the B wave's own weight matrix (GATEUP: wave 3 reads W3, wave 2 W1), as
   // one resource built from a pointer chosen up front (a select between two
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       const int r = ((wave & 1) * C::NIB + j) * C::ROWS_PER_INST_B + lane / C::CPRB;
       const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
       const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + min(r, 255);
-      voff[j] = n < N ? (uint32_t)(((int64_t)n * K + kbeg_el) * WB + chunk * 16) : kOobOff;
+      voff[j] = n < N ? (uint32_t)(((int64_t)n * K + kbeg_el) * WBITS / 8 + chunk * 16) : kOobOff;
     }
   });
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
@@ -559,8 +569,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   static_for<HPS>([&](auto h) {
     static_for<2>([&](auto kk) { col_off[h][kk] = (((h * 4 + kk * 2 + fhalf) ^ swz) * 16); });
   });
-  // fp8 weight rows: 8 codes (8 bytes) per fragment, half of a swizzled
-  // 16-byte chunk; the B tile rows are 32-aligned as well
+  // quantised weight rows: 8 codes (8 or 4 bytes) per fragment, part of a
+  // swizzled 16-byte chunk; the B tile rows are 32-aligned as well
   const int swzb = FP8 ? (frow / C::RPSB) % C::CPRB : 0;
   // step boundary before slice sl (sl % HPS == 0, sl > 0): see above
   // a wave's DMA instructions per step: NI (activation waves) or NIB (weight
@@ -592,7 +602,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     constexpr int NGA = NG > 0 ? NG : 1;
     // weight fragments: bf16, or the raw fp8 codes, widened just before their
     // MFMAs (so the LDS reads of the next slice need not land early)
-    using BFrag = std::conditional_t<FP8, uint2, bf16x8>;
+    using BFrag = std::conditional_t<WBITS == 16, bf16x8, std::conditional_t<WBITS == 8, uint2, uint32_t>>;
     bf16x8 fa0[2][NGA], fa1[2][NGA];
     BFrag fb0[2][4], fb1[2][4];
     auto read_slice = [&](int sl, bf16x8 (&fa)[2][NGA], BFrag (&fb)[2][4]) __attribute__((always_inline)) {
@@ -610,9 +620,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
             for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
           } else {
-            const int cb = ((h * 2 + kk) ^ swzb) * 16 + fhalf * 8;
+            // the lane's 8 codes: K offset h*32 + kk*16 + fhalf*8 of the step
+            const int bo = (h * 32 + kk * 16 + fhalf * 8) * WBITS / 8;
+            const int cb = (((bo >> 4) ^ swzb) << 4) + (bo & 15);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fb[kk][j] = *(const uint2*)(b + (brow[j] + frow) * C::RBB + cb);
+            for (int j = 0; j < 4; ++j) fb[kk][j] = *(const BFrag*)(b + (brow[j] + frow) * C::RBB + cb);
           }
         });
       }
@@ -638,8 +650,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const bf16x8 bv = WQ == WQ_INT8 ? int8x8_to_bf16x8(fb[kk][j])
-                                              : fp8x8_to_bf16x8(fb[kk][j]);
+              bf16x8 bv;
+              if constexpr (WQ == WQ_INT4)
+                bv = int4x8_to_bf16x8(fb[kk][j]);
+              else if constexpr (WQ == WQ_INT8)
+                bv = int8x8_to_bf16x8(fb[kk][j]);
+              else
+                bv = fp8x8_to_bf16x8(fb[kk][j]);
 #pragma unroll
               for (int i = 0; i < NG; ++i) {
                 if (MODE == MODE_GATEUP)
@@ -872,7 +889,7 @@ inline unsigned sched_grid(const GemmParams& p) {
 template <int MODE, int WQ, int KB, int NS>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  using C = DmaCfg<KB, NS, WQ != WQ_BF16>;
+  using C = DmaCfg<KB, NS, wq_bits(WQ)>;
   const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ>;
   static int slots = 0;
   if (!slots) {
@@ -899,10 +916,13 @@ hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
   if (deep) {
     if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 32, 3>(p, st);
     if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 32, 3>(p, st);
+    // 4-bit rows of a 32-deep step are 16 bytes: one chunk, as the DMA needs
+    if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 32, 3>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3>(p, st);
   }
   if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
   if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
+  if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 2>(p, st);
   return launch_gemm_dma<MODE, WQ_BF16, 64, 2>(p, st);
 }
 
@@ -928,7 +948,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
     if (err == hipSuccess && ev_mid) err = hipEventRecord(ev_mid, st);
     return err;
   }
-  const int wq = s.w_dtype == MOE_DT_FP8_E4M3 ? WQ_FP8 : (s.w_dtype == MOE_DT_INT8 ? WQ_INT8 : WQ_BF16);
+  const int wq = s.w_dtype == MOE_DT_FP8_E4M3 ? WQ_FP8
+                 : s.w_dtype == MOE_DT_INT8   ? WQ_INT8
+                 : s.w_dtype == MOE_DT_INT4   ? WQ_INT4
+                                              : WQ_BF16;
   const int has_sh = s.has_shared ? 1 : 0;
   float* tail_slab = H ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
   const int tail_cap = L.tail_cap;

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (DT_BF16, DT_F32, DT_FP8_E4M3, DT_INT8, LINEAR_BIAS, SWIGLU, make_shape, make_weights,
+from . import (DT_BF16, DT_F32, DT_FP8_E4M3, DT_INT4, DT_INT8, LINEAR_BIAS, SWIGLU, make_shape, make_weights,
                moe_forward, moe_workspace_bytes)
 
 
@@ -27,7 +27,8 @@ class MoELayer:
                  reroute_rounds=0, n_groups=0, topk_groups=0, device="cuda"):
         self.kind = SWIGLU if kind == "swiglu" else LINEAR_BIAS
         act = DT_BF16 if self.kind == SWIGLU else DT_F32
-        wdt = {"bf16": DT_BF16, "fp8_e4m3": DT_FP8_E4M3, "int8": DT_INT8, "f32": DT_F32}[w_dtype]
+        wdt = {"bf16": DT_BF16, "fp8_e4m3": DT_FP8_E4M3, "int8": DT_INT8, "int4": DT_INT4,
+               "f32": DT_F32}[w_dtype]
         self.shape = make_shape(T, d, E, top_k, d_ff, capacity, act, wdt, self.kind, has_shared,
                                 overflow, reroute_rounds, n_groups, topk_groups)
         self.W_g = W_g

@@ -79,7 +79,7 @@ def test_workspace_bytes_degenerate(moe, T, d, E, k):
     (dict(T=-1), "T="), (dict(E=0), "E="), (dict(top_k=9), "top_k"), (dict(top_k=0), "top_k"),
     (dict(capacity=-2), "capacity"), (dict(d=0), "d="), (dict(d=100), "multiple of 64"),
     (dict(d_ff=100), "d_ff"), (dict(act_dtype=0), "bf16 x"), (dict(w_dtype=0), "weights"),
-    (dict(kind=7), "kind"), (dict(overflow=3), "overflow="),
+    (dict(w_dtype=5), "weights"), (dict(kind=7), "kind"), (dict(overflow=3), "overflow="),
     (dict(reroute_rounds=-1), "reroute_rounds"), (dict(reroute_rounds=1025), "reroute_rounds"),
     (dict(overflow=2), "has_shared"), (dict(n_groups=3, topk_groups=1), "divide"),
     (dict(n_groups=4, topk_groups=0), "topk_groups"), (dict(n_groups=4, topk_groups=5), "topk_groups"),
@@ -98,6 +98,15 @@ def test_validation_rejects_bad_shapes(moe, kw, needle):
     assert needle in str(ei.value)
 
 
+def test_int4_weights_need_scales(moe):
+    """int4 weights are accepted as a SwiGLU weight type and, like the other
+    quantised types, need their per-128-row scales."""
+    s = moe.make_shape(16, 256, 8, 2, 128, w_dtype=moe.DT_INT4)
+    with pytest.raises(moe.MoEError, match="s1 is NULL"):
+        moe.moe_forward(s, 256, 256, None, moe.make_weights(W1=256, W3=256, W2=256), 256, 256,
+                        256, 256, 256, 256, stream=0)
+
+
 def test_validation_null_and_alignment(moe):
     s = moe.make_shape(16, 256, 8, 2, 128)
     with pytest.raises(moe.MoEError, match="x is NULL"):
@@ -109,8 +118,13 @@ def test_validation_null_and_alignment(moe):
     with pytest.raises(moe.MoEError, match="exactly one"):
         moe.moe_expert_ffn(s, moe.make_weights(W1=256, W3=256, W2=256), 256, 256, 256, 256,
                            None, None, 256, stream=0)
-    with pytest.raises(moe.MoEError, match="E <= 256"):
-        moe.moe_route(moe.make_shape(16, 256, 512, 2, 128), 256, 256, None, None, 256, 256, 256,
+    # more than 256 experts: bf16 x with d % 32 == 0 only
+    with pytest.raises(moe.MoEError, match="more than 256 experts"):
+        moe.moe_route(moe.make_shape(16, 256, 512, 2, 0, act_dtype=moe.DT_F32, w_dtype=moe.DT_F32,
+                                     kind=moe.LINEAR_BIAS), 256, 256, None, None, 256, 256, 256,
+                      stream=0)
+    with pytest.raises(moe.MoEError, match="more than 256 experts"):
+        moe.moe_route(moe.make_shape(16, 272, 512, 2, 128), 256, 256, None, None, 256, 256, 256,
                       stream=0)
     with pytest.raises(moe.MoEError, match="shared"):
         moe.moe_forward(moe.make_shape(16, 8, 4, 2, 0, -1, 0, 0, 0, True), 256, 256, None,

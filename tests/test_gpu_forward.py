@@ -63,6 +63,14 @@ SMALL = [
     (64, 512, 8, 2, 1408, None, False, "int8", None),
     (96, 256, 16, 2, 384, 0.75, True, "int8", "zipf1.5"),
     (600, 512, 4, 2, 4096, None, False, "int8", None),
+    # int4 weights (two codes per byte): the same shapes, so both pipeline
+    # shapes (16-byte weight rows per 32-deep step, 32-byte per 64-deep),
+    # split tail tiles and the shared expert are covered
+    (1100, 512, 8, 2, 384, None, True, "int4", None),
+    (64, 512, 8, 2, 1408, None, False, "int4", None),
+    (96, 256, 16, 2, 384, 0.75, True, "int4", "zipf1.5"),
+    (600, 512, 4, 2, 4096, None, False, "int4", None),
+    (300, 4096, 4, 2, 256, None, True, "int4", None),
 ]
 
 
@@ -182,7 +190,8 @@ def _sample_tokens(T, n, seed):
 
 @pytest.mark.parametrize("name,nsample", [("mixtral", 40), ("decode", 64),
                                           ("capacity_skew", 40), ("fine_grained", 12),
-                                          ("fine_grained_fp8", 12), ("fine_grained_int8", 12)])
+                                          ("fine_grained_fp8", 12), ("fine_grained_int8", 12),
+                                          ("fine_grained_int4", 12)])
 def test_workload_full_size(moe, name, nsample):
     print(f"[workload] {name}", flush=True)
     wl = Workload(get_config(name))

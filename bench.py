@@ -236,6 +236,23 @@ def main() -> int:
                        "lpt_8_max_over_mean": max(bins) / (sum(bins) / len(bins))}
     result["load_stats"] = stats
 
+    # ---- weight stream: the bytes of the experts this step touched (codes
+    # and scales in the workload's weight format, the shared expert included)
+    # against the step time and against the two FFN stages
+    if cfg.kind == "swiglu":
+        wbits = {"bf16": 16, "fp8_e4m3": 8, "int8": 8, "int4": 4}[cfg.w]
+        per_expert = 3 * cfg.d * cfg.d_ff * wbits // 8
+        if wbits != 16:
+            per_expert += 4 * (2 * cfg.d_ff + cfg.d) // 128
+        n_exp = sum(1 for v in kept_rows if v > 0) + (1 if cfg.shared else 0)
+        wb = n_exp * per_expert
+        ffn_ms = gu_ms + dn_ms
+        result["weight_stream"] = {
+            "experts": n_exp, "bytes": wb,
+            "gbs_over_step": wb / (ms_per_step * 1e-3) / 1e9,
+            "hbm_frac_over_step": wb / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "gbs_over_ffn_stages": wb / (ffn_ms * 1e-3) / 1e9}
+
     # ---- online EPLB on the device: replicas + placement onto 8 devices from
     # this step's counts (still on the device), E/8 extra replicas
     D, extra = 8, max(1, cfg.E // 8)

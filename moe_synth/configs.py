@@ -51,6 +51,9 @@ CONFIGS = {
     "decode": MoEConfig("decode", T=64, d=4096, E=8, k=2, d_ff=14336,
                         kind="swiglu", act="bf16", w="bf16", seed=SEED_BASE + 2,
                         x_from="mixtral", w_from="mixtral"),
+    "decode_int4": MoEConfig("decode_int4", T=64, d=4096, E=8, k=2, d_ff=14336,
+                             kind="swiglu", act="bf16", w="int4", seed=SEED_BASE + 2,
+                             x_from="mixtral", w_from="mixtral"),
     "fine_grained": MoEConfig("fine_grained", T=4096, d=7168, E=256, k=8,
                               d_ff=2048, kind="swiglu", act="bf16", w="bf16",
                               shared=True, seed=SEED_BASE + 4),

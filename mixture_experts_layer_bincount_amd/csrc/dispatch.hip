@@ -22,6 +22,8 @@
 //                 rank is the popcount of lower such lanes; waves are ordered
 //                 through an LDS table.  Writes perm_token / perm_w /
 //                 slot_pos / keep.
+// When all assignments fit one chunk, one workgroup does all three steps in
+// a single launch (dispatch_one_chunk_kernel).
 #include "moe_internal.h"
 
 namespace moe {
@@ -196,6 +198,78 @@ __global__ __launch_bounds__(256) void rank_kernel(
   });
 }
 
+// All assignments in one chunk (decode-sized batches): the histogram, the
+// scan over experts and the stable ranks of the three kernels above in one
+// workgroup and one launch.  LDS: (8 E + 256) int32.
+__global__ __launch_bounds__(256) void dispatch_one_chunk_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t A, int k, int E,
+    int ebits, int chunk, int C, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ perm_token, float* __restrict__ perm_w,
+    int32_t* __restrict__ slot_pos) {
+  extern __shared__ int32_t sm[];
+  int32_t* soff = sm + 5 * E;  // [E] the experts' first grouped rows
+  int32_t* zb = sm + 6 * E;    // [E] zeros: no earlier chunks
+  int32_t* h = sm + 7 * E;     // [E] histogram
+  int32_t* ss = sm + 8 * E;    // [256] scan of the per-thread sums
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    h[e] = 0;
+    zb[e] = 0;
+  }
+  __syncthreads();
+  for (int64_t a = tid; a < A; a += 256) {
+    const int e = idx[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of kept = min(count, C) over the experts: thread tid owns
+  // experts tid * per .. tid * per + per - 1
+  const int per = (E + 255) / 256;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) sum += (C < 0) ? h[e] : min(h[e], C);
+  }
+  ss[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t v = (tid >= off) ? ss[tid - off] : 0;
+    __syncthreads();
+    ss[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = ss[tid] - sum;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      counts[e] = h[e];
+      soff[e] = run;
+      offsets[e] = run;
+      run += (C < 0) ? h[e] : min(h[e], C);
+    }
+  }
+  if (tid == 255) offsets[E] = ss[255];
+  float wv[kSubRounds];
+#pragma unroll
+  for (int r = 0; r < kSubRounds; ++r) {
+    const int64_t a = r * 256 + tid;
+    wv[r] = (a < A) ? w[a] : 0.f;
+  }
+  __syncthreads();  // soff, zb written
+  rank_chunk(idx, A, E, ebits, chunk, zb, sm, [&](int64_t a, int r, int e, int32_t rank) {
+    const bool kp = e >= 0 && ((C < 0) || (rank < C));
+    if (kp) {
+      const int32_t pos = soff[e] + rank;
+      perm_token[pos] = (int32_t)(a / k);
+      perm_w[pos] = wv[r];
+      slot_pos[a] = pos;
+    } else {
+      slot_pos[a] = -1;
+    }
+    if (keep) keep[a] = kp ? 1 : 0;
+  });
+}
+
 // ---------------------------------------------------------------- re-routing
 // fde-learning "MoE 并行" (推理时的负载均衡): an assignment past its expert's
 // capacity goes to its token's next expert.  State per assignment: fin[a] =
@@ -338,6 +412,12 @@ hipError_t launch_dispatch(const moe_shape& s, const WsLayout& L, const int32_t*
   const int chunk = dispatch_chunk(s.top_k);
   int ebits = 0;
   while ((1 << ebits) < s.E) ++ebits;
+  if (!hist_ready && L.nchunks == 1) {
+    dispatch_one_chunk_kernel<<<1, 256, (8 * s.E + 256) * sizeof(int32_t), st>>>(
+        topk_idx, topk_w, A, s.top_k, s.E, ebits, chunk, s.capacity, counts, offsets, keep,
+        perm_token, perm_w, slot_pos);
+    return hipGetLastError();
+  }
   if (!hist_ready)
     hist_kernel<<<L.nchunks, 256, s.E * sizeof(int32_t), st>>>(topk_idx, A, s.E, chunk,
                                                                chunk_hist);

@@ -780,6 +780,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   if (r >= rem || S <= 1) return;
   TileMap t;
   tile_place<BM>(p, s_pre, qtail + r, t);
+  if (band * ROWS >= t.rows - t.m0) return;  // the band holds no rows of the segment
   const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * 65536;
   const int64_t obase = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
   // ROWS x 256 floats per band: 16 rows x 64 float4 = 4 float4 per thread;

@@ -27,9 +27,10 @@ scale per group of 128 output features: s = amax(group)/448 and
 code = RNE(w/s), via torch's float8_e4m3fn conversion.  The int8 workload
 uses symmetric int8 codes with the same grouping: s = amax(group)/127 and
 code = RNE(w/s) in float32, clipped to [-127, 127].  The int4 workload does
-the same with s = amax(group)/7 and codes clipped to [-7, 7], packed two per
-byte along the input dimension (even index in the low nibble) into the
-one-field structured dtype INT4X2.  This is weight preparation of the input,
+the same with s = amax(group)/7 and codes clipped to [-7, 7], stored as
+offset-binary nibbles c = n + 8: each group of 8 consecutive inputs takes 4
+bytes, byte b holding input b in its low nibble and input b + 4 in its high
+nibble, in the one-field structured dtype INT4X2.  This is weight preparation of the input,
 not part of the layer.
 """
 from __future__ import annotations
@@ -103,9 +104,9 @@ def _quant_int4_rows(w_bf16: np.ndarray):
     g = w.reshape(out // FP8_GROUP, FP8_GROUP, inn)
     amax = np.maximum(np.abs(g).max(axis=(1, 2)), np.float32(1e-30))
     s = (amax / np.float32(INT4_MAX)).astype(np.float32)
-    q = np.clip(np.rint(g / s[:, None, None]), -INT4_MAX, INT4_MAX).astype(np.int8)
-    u = q.reshape(out, inn).view(np.uint8) & np.uint8(0xF)
-    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    q = np.clip(np.rint(g / s[:, None, None]), -INT4_MAX, INT4_MAX).astype(np.int16)
+    c = (q.reshape(out, inn // 8, 8) + 8).astype(np.uint8)      # offset binary
+    packed = (c[:, :, 0:4] | (c[:, :, 4:8] << np.uint8(4))).reshape(out, inn // 2)
     return np.ascontiguousarray(packed).view(INT4X2), s
 
 

@@ -691,38 +691,54 @@ def test_int8_dequant_definition_and_torch():
 
 
 def test_int4_dequant_hand_worked_bytes():
-    """Packed int4 (two codes per byte, even input index in the low nibble,
-    4-bit two's complement), worked by hand: 0x10 -> (0, 1), 0xF7 -> (7, -1),
-    0x8F -> (-1, -8), 0x00 -> (0, 0); rows 128.. take the second scale."""
-    b = np.array([[0x10, 0xF7, 0x8F, 0x00]] * 256, dtype=np.uint8).view(oracle.INT4X2)
+    """Packed int4, worked by hand: offset-binary codes (c = n + 8), the 8
+    inputs of a group in 4 bytes, byte b holding input b (low nibble) and
+    input b + 4 (high nibble).  Bytes 08 F9 17 80 hold c = 8, 9, 7, 0 | 0,
+    15, 1, 8, i.e. n = 0, 1, -1, -8, -8, 7, -7, 0; rows 128.. take the second
+    scale."""
+    b = np.array([[0x08, 0xF9, 0x17, 0x80]] * 256, dtype=np.uint8).view(oracle.INT4X2)
     W = oracle.dequant_int4_rows(b, np.array([0.5, 2.0], np.float32))
     assert W.shape == (256, 8)
-    assert W[0].tolist() == [0.0, 0.5, 3.5, -0.5, -0.5, -4.0, 0.0, 0.0]
-    assert W[255].tolist() == [0.0, 2.0, 14.0, -2.0, -2.0, -16.0, 0.0, 0.0]
+    assert W[0].tolist() == [0.0, 0.5, -0.5, -4.0, -4.0, 3.5, -3.5, 0.0]
+    assert W[255].tolist() == [0.0, 2.0, -2.0, -16.0, -16.0, 14.0, -14.0, 0.0]
 
 
-def test_int4_unpack_all_bytes_by_arithmetic_shift():
-    """Every byte value: the low code is the byte shifted left by 4 then
-    arithmetically right by 4 as an int8, the high code the byte as an int8
-    shifted arithmetically right by 4 (numpy's sign-extending shifts)."""
-    allb = np.arange(256, dtype=np.uint8).reshape(1, 256)
-    got = oracle.unpack_int4(allb.view(oracle.INT4X2))
-    lo = (allb << np.uint8(4)).view(np.int8) >> np.int8(4)
-    hi = allb.view(np.int8) >> np.int8(4)
-    assert np.array_equal(got[:, 0::2], lo.astype(np.int64))
-    assert np.array_equal(got[:, 1::2], hi.astype(np.int64))
+def test_int4_unpack_all_bytes_by_bits():
+    """Every byte value at every position of a group: the codes read from the
+    byte's bits (numpy's unpackbits, most significant first) minus 8."""
+    # row r, byte 4g + b holds (4g + b + r) mod 256: every value at every
+    # byte position of a group, over the four rows
+    packed = ((np.arange(256)[None, :] + np.arange(4)[:, None]) % 256).astype(np.uint8)
+    got = oracle.unpack_int4(packed.view(oracle.INT4X2))
+    bits = np.unpackbits(packed[:, :, None], axis=2).astype(np.int64)   # [4, 256, 8]
+    hi = bits[:, :, 0:4] @ np.array([8, 4, 2, 1]) - 8
+    lo = bits[:, :, 4:8] @ np.array([8, 4, 2, 1]) - 8
+    for r in range(4):
+        for byte in range(256):
+            g, bpos = divmod(byte, 4)
+            assert got[r, 8 * g + bpos] == lo[r, byte]
+            assert got[r, 8 * g + bpos + 4] == hi[r, byte]
+    for bpos in range(4):
+        assert sorted(packed[:, bpos::4].ravel().tolist()) == list(range(256))
 
 
 def test_int4_reduces_to_int8_and_synthetic_round_trip():
-    """Codes in [-7, 7] packed as int4 decode to the same weights as the
-    same codes stored as int8; the synthetic quantiser keeps |code| <= 7
-    (7 reached in every group) with round-trip error <= scale / 2."""
+    """Codes in [-7, 7] packed as int4 (by the definition, one nibble at a
+    time) decode to the same weights as the same codes stored as int8; the
+    synthetic quantiser keeps |code| <= 7 (7 reached in every group) with
+    round-trip error <= scale / 2."""
     rng = np.random.default_rng(11)
     codes = rng.integers(-7, 8, size=(256, 64)).astype(np.int8)
-    u = codes.view(np.uint8) & np.uint8(0xF)
-    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).view(oracle.INT4X2)
+    packed = np.zeros((256, 32), dtype=np.uint8)
+    for r in range(256):
+        for k in range(64):
+            g, j = divmod(k, 8)
+            byte = 4 * g + (j % 4)
+            c = int(codes[r, k]) + 8
+            packed[r, byte] |= c if j < 4 else c << 4
     s = np.array([0.125, 3.0], np.float32)
-    assert np.array_equal(oracle.dequant_int4_rows(packed, s), oracle.dequant_int8_rows(codes, s))
+    assert np.array_equal(oracle.dequant_int4_rows(packed.view(oracle.INT4X2), s),
+                          oracle.dequant_int8_rows(codes, s))
     from moe_synth.gen import _quant_int4_rows, f32_to_bf16_bits, bf16_bits_to_f32
     w = f32_to_bf16_bits(rng.standard_normal((256, 64)).astype(np.float32))
     q, sc = _quant_int4_rows(w)

@@ -77,10 +77,11 @@ typedef enum moe_dtype {
   MOE_DT_FP8_E4M3 = 2, /* OCP FP8 E4M3 (bias 7, max 448, no infinities) */
   MOE_DT_INT8 = 3,     /* symmetric int8 codes -127..127 (iopenshare §5.3: INT8 expert
                           weights); weight = code * scale */
-  MOE_DT_INT4 = 4      /* symmetric int4 codes -7..7 (iopenshare §5.3: INT4 expert weights),
-                          two per byte along the input dimension, the even input index
-                          in the low nibble; a nibble is two's complement (0x8 reads as
-                          -8); weight = code * scale */
+  MOE_DT_INT4 = 4      /* symmetric int4 codes n in -7..7 (iopenshare §5.3: INT4 expert
+                          weights; -8 is also accepted), each stored as the nibble
+                          c = n + 8; along a weight row every group of 8 inputs takes 4
+                          bytes, byte b holding input b in its low nibble and input b + 4
+                          in its high nibble; weight = n * scale */
 } moe_dtype;
 
 typedef enum moe_expert_kind {

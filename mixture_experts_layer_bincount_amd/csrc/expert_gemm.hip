@@ -232,11 +232,13 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
 // activation row in the tile, its i-th 32-row granule starting RS rows
 // further per i (32: contiguous rows, 64: granules interleaved with the other
 // row wave); brow: its four 32-row weight tiles; n0: first output column of
-// the tile; wn: the wave's column group.
-template <int MODE, bool FP8, int RS, int BMT>
+// the tile; wn: the wave's column group.  CORR (int4 weights): ctab[i * 32
+// + R] is the amount to take off every accumulator of row R of granule i
+// (136 times the row's activation sum), before the scale.
+template <int MODE, bool FP8, int RS, int BMT, bool CORR = false>
 __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
                                            const TileMap& t, int arow0, int n0, int wn,
-                                           const int (&brow)[4]) {
+                                           const int (&brow)[4], const float* ctab = nullptr) {
   const int lane = threadIdx.x & 63;
   const int ccol = lane & 31;
   const int rbase = (lane >> 5) * 4;
@@ -250,6 +252,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
       __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
       const int m = t.m0 + arow0 + i * RS + ccol;
       if (m >= t.rows) continue;
+      const float cr = CORR ? ctab[i * 32 + ccol] : 0.f;
       uint16_t* hrow = p.H + (hbase + m) * N;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -265,18 +268,19 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
           }
           if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
             float* sl = p.tail_slab + (int64_t)t.slab * 65536 + (int64_t)(m - t.m0) * 256 + (n - n0);
-            *(float4*)sl = make_float4(acc[i][j][q * 4] * sg, acc[i][j][q * 4 + 1] * sg,
-                                       acc[i][j][q * 4 + 2] * sg, acc[i][j][q * 4 + 3] * sg);
-            *(float4*)(sl + 128) =
-                make_float4(acc[i][j + 2][q * 4] * su, acc[i][j + 2][q * 4 + 1] * su,
-                            acc[i][j + 2][q * 4 + 2] * su, acc[i][j + 2][q * 4 + 3] * su);
+            *(float4*)sl = make_float4(
+                (acc[i][j][q * 4] - cr) * sg, (acc[i][j][q * 4 + 1] - cr) * sg,
+                (acc[i][j][q * 4 + 2] - cr) * sg, (acc[i][j][q * 4 + 3] - cr) * sg);
+            *(float4*)(sl + 128) = make_float4(
+                (acc[i][j + 2][q * 4] - cr) * su, (acc[i][j + 2][q * 4 + 1] - cr) * su,
+                (acc[i][j + 2][q * 4 + 2] - cr) * su, (acc[i][j + 2][q * 4 + 3] - cr) * su);
             continue;
           }
           uint32_t hb[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float a = acc[i][j][q * 4 + r] * sg;
-            const float g = acc[i][j + 2][q * 4 + r] * su;
+            const float a = (acc[i][j][q * 4 + r] - cr) * sg;
+            const float g = (acc[i][j + 2][q * 4 + r] - cr) * su;
             hb[r] = f32_to_bf16_bits(a / (1.f + __expf(-a)) * g);
           }
           uint2 v;
@@ -297,6 +301,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
         for (int r = 0; r < 4; ++r) {
           const int m = t.m0 + arow0 + i * RS + q * 8 + rbase + r;
           if (m >= t.rows) continue;
+          const float cr = CORR ? ctab[i * 32 + q * 8 + rbase + r] : 0.f;
           float wgt = 1.f;
           int64_t orow;
           if (MODE == MODE_DOWN) {
@@ -314,7 +319,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
           for (int j = 0; j < 4; ++j) {
             const int n = n0 + brow[j] + ccol;
             if (n >= N) continue;
-            float v = acc[i][j][q * 4 + r];
+            float v = acc[i][j][q * 4 + r] - cr;
             if (FP8) {
               const int gi = n / kFp8Group;
               v *= t.shared_e ? p.sc0s[gi] : p.sc0[(int64_t)t.e * (N / kFp8Group) + gi];
@@ -420,17 +425,43 @@ __device__ __forceinline__ bf16x8 int8x8_to_bf16x8(uint2 q) {
   return r;
 }
 
-// 8 symmetric int4 codes (K order, low nibble first) -> 8 bf16, exactly.
+// One group of 8 int4 codes (offset binary c = n + 8; byte b holds input b
+// in its low nibble and input b + 4 in its high nibble) -> the 8 bf16 values
+// 128 + c = 136 + n, exactly: the bf16 pattern 0x43cc is 128 + c for c < 16,
+// so after splitting the nibbles into bytes each pair of values is one byte
+// permute with the constant 0x43.  The MFMA then sums a * (136 + n); the
+// epilogue takes 136 * (sum of a) off (int4_rowsum below).
 __device__ __forceinline__ bf16x8 int4x8_to_bf16x8(uint32_t q) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)((int32_t)(q << (28 - 4 * i)) >> 28);
-  return r;
+  const uint32_t lo = q & 0x0F0F0F0Fu;         // c of inputs 0..3, one per byte
+  const uint32_t hi = (q >> 4) & 0x0F0F0F0Fu;  // c of inputs 4..7
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v r;
+  // v_perm_b32: selector bytes 0..3 pick bytes of the second source, 4..7
+  // bytes of the first (the constant)
+  r.x = __builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+// The offset the int4 widening adds to every code.
+constexpr float kInt4Offset = 136.f;
+
+// Sum of the 8 bf16 activations of a fragment, added to acc (fp32 dot
+// products with ones).
+__device__ __forceinline__ float int4_rowsum(bf16x8 a, float acc) {
+  typedef __bf16 bf16x2v2 __attribute__((ext_vector_type(2)));
+  const bf16x2v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), one, acc, false);
+  return acc;
 }
 
 // Weight formats of the GEMM: bf16, or 8-bit / 4-bit codes with fp32 scales
-// per 128 output rows (OCP fp8 e4m3, symmetric int8, symmetric int4 packed
-// two per byte, low nibble first).
+// per 128 output rows (OCP fp8 e4m3, symmetric int8, symmetric int4 as
+// offset-binary nibbles in groups of 8 inputs).
 enum { WQ_BF16 = 0, WQ_FP8 = 1, WQ_INT8 = 2, WQ_INT4 = 3 };
 constexpr int wq_bits(int wq) { return wq == WQ_BF16 ? 16 : (wq == WQ_INT4 ? 4 : 8); }
 
@@ -557,6 +588,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   wave_brows<MODE, BNB>(wn, brow);
   f32x16 acc[4][4];
   zero_acc(acc);
+  // int4: the lane's partial sums of its activation rows over its K halves
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
   const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
   const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
 
@@ -664,12 +697,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               bf16x8 bv;
-              if constexpr (WQ == WQ_INT4)
+              if constexpr (WQ == WQ_INT4) {
                 bv = int4x8_to_bf16x8(fb[kk][j]);
-              else if constexpr (WQ == WQ_INT8)
+                // the row sums ride on the j loop: granule j's fragment
+                if (j < NG) rs[j] = int4_rowsum(fa[kk][j], rs[j]);
+              } else if constexpr (WQ == WQ_INT8) {
                 bv = int8x8_to_bf16x8(fb[kk][j]);
-              else
+              } else {
                 bv = fp8x8_to_bf16x8(fb[kk][j]);
+              }
 #pragma unroll
               for (int i = 0; i < NG; ++i) {
                 if (MODE == MODE_GATEUP)
@@ -721,7 +757,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     else
       run(std::integral_constant<int, 0>{});
   }
-  store_tile<MODE, FP8, 64, DMA_BM>(p, acc, t, arow0, n0, wn, brow);
+  if constexpr (WQ == WQ_INT4) {
+    // full row sums (the lane pair l, l ^ 32 holds the two K halves of row
+    // l & 31 of each granule), times the widening's offset, per wave in LDS
+    __shared__ float s_corr[4][4][32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float full = rs[i] + __shfl_xor(rs[i], 32);
+      if (lane < 32) s_corr[wave][i][lane] = kInt4Offset * full;
+    }
+    __syncthreads();
+    store_tile<MODE, FP8, 64, DMA_BM, true>(p, acc, t, arow0, n0, wn, brow, &s_corr[wave][0][0]);
+  } else {
+    store_tile<MODE, FP8, 64, DMA_BM>(p, acc, t, arow0, n0, wn, brow);
+  }
 }
 
 // Linear+bias experts in fp32 (the tutorial's nn.Linear(d, d) experts, §4.1).

@@ -234,8 +234,10 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
 // row wave); brow: its four 32-row weight tiles; n0: first output column of
 // the tile; wn: the wave's column group.  CORR (int4 weights): ctab[i * 32
 // + R] is the amount to take off every accumulator of row R of granule i
-// (136 times the row's activation sum), before the scale.
-template <int MODE, bool FP8, int RS, int BMT, bool CORR = false>
+// (136 times the row's activation sum), before the scale.  GI: the wave's
+// granules in the tile (4 in a 256-row tile, 1 in a 64-row one); rows past
+// them belong to the next tile.
+template <int MODE, bool FP8, int RS, int BMT, bool CORR = false, int GI = 4>
 __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
                                            const TileMap& t, int arow0, int n0, int wn,
                                            const int (&brow)[4], const float* ctab = nullptr) {
@@ -248,7 +250,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
     // row arow0 + i*RS + ccol; tiles j and j + 2 are the gate and up halves.
     const int64_t hbase = t.shared_e ? p.P_max : (int64_t)t.seg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < GI; ++i) {
       __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
       const int m = t.m0 + arow0 + i * RS + ccol;
       if (m >= t.rows) continue;
@@ -293,7 +295,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
   } else {
     // acc[i][j]: activation row arow0 + i*RS + R, output column brow[j] + ccol.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < GI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
@@ -371,15 +373,15 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 constexpr int DMA_BM = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int KB, int NS, int WBITS>
+template <int KB, int NS, int WBITS, int BMA = 256>
 struct DmaCfg {
   // activation (A) tile: 256 rows of KB bf16
   static constexpr int RB = KB * 2;                 // bytes per A row and stage
   static constexpr int CPR = RB / 16;               // 16-byte chunks per A row
   static constexpr int RPS = 256 / RB;              // A rows per 256-byte bank sweep
   static constexpr int ROWS_PER_INST = 1024 / RB;   // A rows one wave-level DMA fills
-  static constexpr int NI = 128 / ROWS_PER_INST;    // A DMA instructions per wave and stage
-  static constexpr int TILE_BYTES = 256 * RB;       // the A tile
+  static constexpr int NI = BMA / 2 / ROWS_PER_INST;  // A DMA instructions per wave and stage
+  static constexpr int TILE_BYTES = BMA * RB;         // the A tile (BMA activation rows)
   // weight (B) tile: 256 rows of KB weights of WBITS bits (16 bf16, 8 or 4)
   static constexpr int RBB = KB * WBITS / 8;         // bytes per B row and stage
   static constexpr int CPRB = RBB / 16;
@@ -391,6 +393,7 @@ struct DmaCfg {
   static constexpr int NI_MAX = NI > NIB ? NI : NIB;
   static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
   static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4 && RBB >= 16, "DMA pipeline shape");
+  static_assert((BMA == 256 || BMA == 64) && NI >= 1, "activation tile rows");
   static_assert(LDS <= 150 * 1024, "LDS budget (with the static tile-map arrays)");
 };
 
@@ -479,15 +482,15 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX, int WQ>
+template <int MODE, int KB, int NS, int MOE_AUX, int WQ, int BMA>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   constexpr bool FP8 = WQ != WQ_BF16;  // quantised weight codes with scales
   constexpr int WBITS = wq_bits(WQ);
-  using C = DmaCfg<KB, NS, WBITS>;
+  using C = DmaCfg<KB, NS, WBITS, BMA>;
   constexpr int BNB = 256;
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
   TileMap t;
-  if (!map_tile<MODE, DMA_BM>(p, t)) return;
+  if (!map_tile<MODE, BMA>(p, t)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -521,9 +524,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   uint32_t voff[C::NI_MAX];
   static_for<C::NI_MAX>([&](auto j) {
     if (wave < 2) {
-      const int r = ((wave & 1) * C::NI + j) * C::ROWS_PER_INST + lane / C::CPR;  // 0..255
+      const int r = ((wave & 1) * C::NI + j) * C::ROWS_PER_INST + lane / C::CPR;  // 0..BMA-1
       const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
-      const int m = t.m0 + min(r, 255);
+      const int m = t.m0 + min(r, BMA - 1);
       voff[j] = m < t.rows
                     ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16)
                     : kOobOff;
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   zero_acc(acc);
   // int4: the lane's partial sums of its activation rows over its K halves
   float rs[4] = {0.f, 0.f, 0.f, 0.f};
-  const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
+  const int vg = min(BMA / 32, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
   const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
 
   // fragment reads: tile rows are 32-aligned, so swz(row) = (frow / RPS) % CPR
@@ -746,12 +749,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     if (sl < nsl) slice(fa0, fb0, nsl, fa1, fb1);
   };
   if (nk > 0) {
-    if (ng >= 4)
-      run(std::integral_constant<int, 4>{});
-    else if (ng == 3)
-      run(std::integral_constant<int, 3>{});
-    else if (ng == 2)
-      run(std::integral_constant<int, 2>{});
+    if (BMA > 64 && ng >= 4)
+      run(std::integral_constant<int, (BMA > 64 ? 4 : 1)>{});
+    else if (BMA > 64 && ng == 3)
+      run(std::integral_constant<int, (BMA > 64 ? 3 : 1)>{});
+    else if (BMA > 64 && ng == 2)
+      run(std::integral_constant<int, (BMA > 64 ? 2 : 1)>{});
     else if (ng == 1)
       run(std::integral_constant<int, 1>{});
     else
@@ -767,9 +770,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       if (lane < 32) s_corr[wave][i][lane] = kInt4Offset * full;
     }
     __syncthreads();
-    store_tile<MODE, FP8, 64, DMA_BM, true>(p, acc, t, arow0, n0, wn, brow, &s_corr[wave][0][0]);
+    store_tile<MODE, FP8, 64, DMA_BM, true, BMA / 64>(p, acc, t, arow0, n0, wn, brow,
+                                                      &s_corr[wave][0][0]);
   } else {
-    store_tile<MODE, FP8, 64, DMA_BM>(p, acc, t, arow0, n0, wn, brow);
+    store_tile<MODE, FP8, 64, DMA_BM, false, BMA / 64>(p, acc, t, arow0, n0, wn, brow);
   }
 }
 
@@ -813,15 +817,15 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
 // XCD b % 8, then (tail tile, band) of b / 8 (the same schedule arithmetic
 // as the GEMM, from the same offsets).
 constexpr int kFixBands = 16;
-template <int MODE>
+template <int MODE, int BM>
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
-  constexpr int BM = DMA_BM;
-  constexpr int ROWS = BM / kFixBands;  // rows per band
+  constexpr int ROWS = DMA_BM / kFixBands;  // rows per band (16)
   __shared__ int s_scan[4];
   __shared__ int s_pre[kMaxSegments + 1];
   const int xcd = (int)(blockIdx.x % kNumXcd);
   const int r = (int)(blockIdx.x / kNumXcd / kFixBands);
   const int band = (int)(blockIdx.x / kNumXcd % kFixBands);
+  if (band * ROWS >= BM) return;  // tiles of BM < 256 rows have fewer bands
   const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
   int64_t qtail = 0;
   int rem = 0, S = 1;
@@ -950,11 +954,11 @@ inline unsigned sched_grid(const GemmParams& p) {
 // with few rows, three stages (two steps in flight: such tiles have little
 // compute to hide the operand latency behind) of 32-deep steps, or of 64-deep
 // ones for 4-bit weights.
-template <int MODE, int WQ, int KB, int NS>
+template <int MODE, int WQ, int KB, int NS, int BMA = 256>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  using C = DmaCfg<KB, NS, wq_bits(WQ)>;
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ>;
+  using C = DmaCfg<KB, NS, wq_bits(WQ), BMA>;
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA>;
   static int slots = 0;
   if (!slots) {
     hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -967,9 +971,11 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   p.slots = slots;
   constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
   if (slab_mode && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
-  grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ><<<sched_grid(p), 256, C::LDS, st>>>(p);
+  // row tiles of BMA rows: sum_e ceil(rows_e / BMA) <= P_max / BMA + E (+ shared)
+  p.mt_max = (int)((p.P_max + BMA - 1) / BMA + p.E + (p.has_shared ? (p.T + BMA - 1) / BMA : 0));
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA><<<sched_grid(p), 256, C::LDS, st>>>(p);
   if (slab_mode && p.split_max > 1)
-    tail_fixup_kernel<MODE><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
+    tail_fixup_kernel<MODE, BMA><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -980,10 +986,11 @@ hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
   if (deep) {
     if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 32, 3>(p, st);
     if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 32, 3>(p, st);
-    // 4-bit weights: 64-deep steps (32-byte weight rows) in three stages fit
-    // (120 KiB) and keep twice the bytes in flight (measured 10% faster than
-    // 32-deep steps at 16 rows per expert)
-    if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 3>(p, st);
+    // 4-bit weights: 64-row activation tiles (16 KiB stages) with 64-deep
+    // steps in three stages (measured at 16 rows per expert: 0.38 -> 0.30 ms
+    // for the layer against 256-row tiles; with bf16 weights the same shape
+    // was slower than three 32-deep stages)
+    if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 3, 64>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3>(p, st);
   }
   if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);

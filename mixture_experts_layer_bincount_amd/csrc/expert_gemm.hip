@@ -984,13 +984,14 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
 template <int MODE>
 hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
   if (deep) {
-    if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 32, 3>(p, st);
-    if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 32, 3>(p, st);
     // 64-row activation tiles: a smaller LDS footprint, so two workgroups
-    // share a CU.  4-bit weights with 64-deep steps in three stages (measured
-    // at 16 rows per expert: 0.38 -> 0.30 ms for the layer against 256-row
-    // tiles); bf16 weights with 32-deep ones (0.591 -> 0.582 ms; 64-deep
-    // steps were slower there)
+    // share a CU.  Quantised weights with 64-deep steps in three stages
+    // (measured at 16 rows per expert against 256-row tiles with 32-deep
+    // steps: the fp8 layer 0.598 -> 0.362 ms, int4 0.38 -> 0.30 ms); bf16
+    // weights with 32-deep ones (0.591 -> 0.582 ms; 64-deep steps, which
+    // leave room for one workgroup per CU only, were slower there)
+    if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 3, 64>(p, st);
+    if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 3, 64>(p, st);
     if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 3, 64>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3, 64>(p, st);
   }

@@ -51,6 +51,12 @@ CONFIGS = {
     "decode": MoEConfig("decode", T=64, d=4096, E=8, k=2, d_ff=14336,
                         kind="swiglu", act="bf16", w="bf16", seed=SEED_BASE + 2,
                         x_from="mixtral", w_from="mixtral"),
+    "decode_fp8": MoEConfig("decode_fp8", T=64, d=4096, E=8, k=2, d_ff=14336,
+                            kind="swiglu", act="bf16", w="fp8_e4m3", seed=SEED_BASE + 2,
+                            x_from="mixtral", w_from="mixtral"),
+    "decode_int8": MoEConfig("decode_int8", T=64, d=4096, E=8, k=2, d_ff=14336,
+                             kind="swiglu", act="bf16", w="int8", seed=SEED_BASE + 2,
+                             x_from="mixtral", w_from="mixtral"),
     "decode_int4": MoEConfig("decode_int4", T=64, d=4096, E=8, k=2, d_ff=14336,
                              kind="swiglu", act="bf16", w="int4", seed=SEED_BASE + 2,
                              x_from="mixtral", w_from="mixtral"),

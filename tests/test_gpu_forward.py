@@ -191,7 +191,8 @@ def _sample_tokens(T, n, seed):
 @pytest.mark.parametrize("name,nsample", [("mixtral", 40), ("decode", 64),
                                           ("capacity_skew", 40), ("fine_grained", 12),
                                           ("fine_grained_fp8", 12), ("fine_grained_int8", 12),
-                                          ("fine_grained_int4", 12), ("decode_int4", 64)])
+                                          ("fine_grained_int4", 12), ("decode_int4", 64),
+                                          ("decode_fp8", 64), ("decode_int8", 64)])
 def test_workload_full_size(moe, name, nsample):
     print(f"[workload] {name}", flush=True)
     wl = Workload(get_config(name))

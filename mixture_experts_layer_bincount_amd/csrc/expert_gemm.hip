@@ -237,7 +237,7 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
 // (136 times the row's activation sum), before the scale.  GI: the wave's
 // granules in the tile (4 in a 256-row tile, 1 in a 64-row one); rows past
 // them belong to the next tile.
-template <int MODE, bool FP8, int RS, int BMT, bool CORR = false, int GI = 4>
+template <int MODE, bool FP8, int RS, int BMT, bool CORR = false, int GI = 4, int TR = 256>
 __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4][4],
                                            const TileMap& t, int arow0, int n0, int wn,
                                            const int (&brow)[4], const float* ctab = nullptr) {
@@ -253,7 +253,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
     for (int i = 0; i < GI; ++i) {
       __builtin_amdgcn_sched_barrier(0);  // keep the accumulator reads incremental
       const int m = t.m0 + arow0 + i * RS + ccol;
-      if (m >= t.rows) continue;
+      if (m >= t.rows || m - t.m0 >= TR) continue;
       const float cr = CORR ? ctab[i * 32 + ccol] : 0.f;
       uint16_t* hrow = p.H + (hbase + m) * N;
 #pragma unroll
@@ -302,7 +302,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = t.m0 + arow0 + i * RS + q * 8 + rbase + r;
-          if (m >= t.rows) continue;
+          if (m >= t.rows || m - t.m0 >= TR) continue;
           const float cr = CORR ? ctab[i * 32 + q * 8 + rbase + r] : 0.f;
           float wgt = 1.f;
           int64_t orow;
@@ -393,7 +393,7 @@ struct DmaCfg {
   static constexpr int NI_MAX = NI > NIB ? NI : NIB;
   static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
   static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4 && RBB >= 16, "DMA pipeline shape");
-  static_assert((BMA == 256 || BMA == 64) && NI >= 1, "activation tile rows");
+  static_assert((BMA == 256 || BMA == 64 || BMA == 32) && NI >= 1, "activation tile rows");
   static_assert(LDS <= 150 * 1024, "LDS budget (with the static tile-map arrays)");
 };
 
@@ -770,10 +770,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       if (lane < 32) s_corr[wave][i][lane] = kInt4Offset * full;
     }
     __syncthreads();
-    store_tile<MODE, FP8, 64, DMA_BM, true, BMA / 64>(p, acc, t, arow0, n0, wn, brow,
+    store_tile<MODE, FP8, 64, DMA_BM, true, (BMA + 63) / 64, BMA>(p, acc, t, arow0, n0, wn, brow,
                                                       &s_corr[wave][0][0]);
   } else {
-    store_tile<MODE, FP8, 64, DMA_BM, false, BMA / 64>(p, acc, t, arow0, n0, wn, brow);
+    store_tile<MODE, FP8, 64, DMA_BM, false, (BMA + 63) / 64, BMA>(p, acc, t, arow0, n0, wn, brow);
   }
 }
 
@@ -982,7 +982,9 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
 
 // Runtime weight format and pipeline shape -> the kernel instantiation.
 template <int MODE>
-hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
+// rows: the average rows per expert (decode-sized batches: 32 or fewer).
+hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st) {
+  const bool deep = rows <= 32;
   if (deep) {
     // 64-row activation tiles: a smaller LDS footprint, so two workgroups
     // share a CU.  Quantised weights with 64-deep steps in three stages
@@ -993,6 +995,10 @@ hipError_t launch_gemm(int wq, bool deep, const GemmParams& p, hipStream_t st) {
     if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 3, 64>(p, st);
     if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 3, 64>(p, st);
     if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 3, 64>(p, st);
+    // bf16 weights at 16 or fewer rows per expert: 32-row tiles with two
+    // 64-deep stages, two workgroups per CU (decode at 16 rows per expert
+    // 0.576 -> 0.542 ms)
+    if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 32>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3, 64>(p, st);
   }
   if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
@@ -1060,14 +1066,15 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // tail tiles split over K through the slab + fixup (SwiGLU needs whole
   // sums), for long K loops only, as in the down projection
   g.split_max = s.d >= 4096 ? std::max(1, s.d / BK / 8) : 1;
-  // few rows per expert (decode-sized batches): the deeper pipeline (measured
-  // 6% faster at 16 rows per expert, slower at 128 and more)
-  const bool deep = L.P_max / s.E <= 32;
+  // few rows per expert (decode-sized batches): smaller activation tiles and
+  // deeper weight pipelines (launch_gemm; slower at 128 rows and more)
+  const int64_t rows_avg = L.P_max / s.E;
+  const bool deep = rows_avg <= 32;
   // 8-bit weights outside decode-sized batches: K rotation (measured on the
   // 256-expert layer: 5-6% faster for fp8 and int8, neutral for int4, slower
   // for bf16 weights and for decode-sized batches)
   g.krot = (!deep && (wq == WQ_FP8 || wq == WQ_INT8)) ? 7 : 0;
-  hipError_t err = launch_gemm<MODE_GATEUP>(wq, deep, g, st);
+  hipError_t err = launch_gemm<MODE_GATEUP>(wq, rows_avg, g, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {
     err = hipEventRecord(ev_mid, st);
@@ -1098,8 +1105,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.tail_slab = tail_slab;
   g2.tail_cap = tail_cap;
   if (y)
-    return launch_gemm<MODE_DOWN>(wq, deep, g2, st);
-  return launch_gemm<MODE_DOWN_PERM>(wq, deep, g2, st);
+    return launch_gemm<MODE_DOWN>(wq, rows_avg, g2, st);
+  return launch_gemm<MODE_DOWN_PERM>(wq, rows_avg, g2, st);
 }
 
 hipError_t launch_combine(const moe_shape& s, int64_t P_max, const float* y_perm,

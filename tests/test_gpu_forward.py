@@ -71,6 +71,13 @@ SMALL = [
     (96, 256, 16, 2, 384, 0.75, True, "int4", "zipf1.5"),
     (600, 512, 4, 2, 4096, None, False, "int4", None),
     (300, 4096, 4, 2, 256, None, True, "int4", None),
+    # decode-sized batches whose skewed routing gives one expert more rows
+    # than the small activation tiles hold (several row tiles per expert)
+    (64, 256, 8, 2, 256, None, False, "bf16", "zipf1.5"),
+    (96, 256, 8, 2, 256, None, True, "bf16", "zipf1.5"),
+    (96, 256, 8, 2, 256, None, True, "fp8_e4m3", "zipf1.5"),
+    (96, 256, 8, 2, 256, None, False, "int8", "zipf1.5"),
+    (96, 256, 8, 2, 256, None, True, "int4", "zipf1.5"),
 ]
 
 

@@ -17,22 +17,24 @@
 //
 // Workgroup tile: 256 activation rows x 256 weight rows, K in steps of 64;
 // 256 threads = 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32x32, 256 fp32
-// accumulators per lane).  A wave's activation rows are the 32-row granules
+// accumulators per lane).  Decode-sized batches (32 or fewer rows per expert
+// on average) use 64- or 32-row activation tiles instead, so two workgroups
+// share a CU.  A wave's activation rows are the 32-row granules
 // wm, wm + 2, wm + 4, wm + 6 of the tile, and it runs only the granules that
 // hold rows of the segment (partial tiles cost in proportion to their rows).
 // In MODE_GATEUP a wave's 128 weight rows are 64 rows of W1 and the same 64
 // rows of W3, so the SwiGLU happens in registers; the product is computed
 // transposed (weights as the MFMA A operand) so each lane holds 4
 // consecutive hidden columns of one row and stores them as one 8-byte write.
-// Operands move global -> LDS by buffer_load ... lds (two 64-deep stages, or
-// three 32-deep ones for decode-sized batches, three 64-deep ones there for
-// 4-bit weights; XOR-swizzled rows, no bank
-// conflicts on the 16-byte fragment reads; no loads for activation rows past
-// the segment's end); the next 32-deep slice's fragments are read under the
-// current slice's MFMAs; one barrier per step.  Quantised weights (OCP fp8
-// e4m3, symmetric int8, or symmetric int4 packed two per byte) land in LDS
-// as codes and are widened exactly to bf16 in registers; their per-128-row
-// scales apply in the epilogue.  With 8-bit weights each workgroup starts its
+// Operands move global -> LDS by buffer_load ... lds (two 64-deep stages;
+// for decode-sized batches two or three stages, see launch_gemm;
+// XOR-swizzled rows, no bank conflicts on the 16-byte fragment reads; no
+// loads for activation rows past the segment's end); the next 32-deep
+// slice's fragments are read under the current slice's MFMAs; one barrier
+// per step.  Quantised weights (OCP fp8 e4m3, symmetric int8, or symmetric
+// int4 as offset-binary nibbles) land in LDS as codes and are widened
+// exactly to bf16 in registers; their per-128-row scales apply in the
+// epilogue.  With 8-bit weights each workgroup starts its
 // K walk at its own offset (K rotation).
 // Tile order (tile_sched.h): the real tiles, counted on the device, are dealt
 // evenly to the XCDs in expert-aligned blocks, so the workgroups one XCD runs
@@ -949,11 +951,12 @@ inline unsigned sched_grid(const GemmParams& p) {
 }
 
 
-// The LDS-DMA kernel.  Pipeline shapes: 64-deep K steps in two stages (one
-// step in flight while one is computed: fewer barriers per K), and, for tiles
-// with few rows, three stages (two steps in flight: such tiles have little
-// compute to hide the operand latency behind) of 32-deep steps, or of 64-deep
-// ones for 4-bit weights.
+// The LDS-DMA kernel: KB-deep K steps in NS stages over tiles of BMA
+// activation rows (launch_gemm picks the shape).  Two 64-deep stages keep
+// one step in flight while one is computed, with few barriers per K; tiles
+// with few rows have little compute to hide the operand latency behind and
+// take smaller activation tiles, which leave LDS for more stages or a second
+// workgroup per CU.
 template <int MODE, int WQ, int KB, int NS, int BMA = 256>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;

@@ -509,10 +509,14 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
     ce.finish();
     return r;
   }
-  MOE_TRY(hip_status(launch_fill_zero(y, s.T * (int64_t)s.d, st), "clear y"));
+  // y starts at zero for the atomic combine: SwiGLU experts clear it inside
+  // the gate/up launch, the Linear+bias ones with a fill kernel
+  const bool swiglu = s.kind == MOE_EXPERT_SWIGLU;
+  if (!swiglu) MOE_TRY(hip_status(launch_fill_zero(y, s.T * (int64_t)s.d, st), "clear y"));
   ce.mark(4, st);
   const moe_status r = hip_status(launch_expert_ffn(s, L, *w, x, offsets, W.perm_token, W.perm_w,
-                                                    nullptr, y, W.H, st, ce.at(5), shared_w),
+                                                    nullptr, y, W.H, st, ce.at(5), shared_w,
+                                                    /*zero_y=*/swiglu),
                                   "expert ffn");
   ce.mark(6, st);
   ce.finish();

@@ -95,6 +95,8 @@ struct GemmParams {
   int tail_cap;               //   (room for tail_cap tiles of 64 Ki floats)
   int group_n;                // weight tiles per expert-aligned block of the tile order
   int krot;                   // K walk start of workgroup b: (b * krot) mod (its K steps); 0 = none
+  float* zero_out;            // zero_n floats (16-byte aligned) the workgroups clear first, or NULL
+  int64_t zero_n;             //   (the atomic combine's y, cleared by the gate/up launch)
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -491,6 +493,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   using C = DmaCfg<KB, NS, WBITS, BMA>;
   constexpr int BNB = 256;
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
+  if (p.zero_out) {  // every workgroup clears its share, with or without a tile
+    const int64_t n4 = p.zero_n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+      ((float4*)p.zero_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < p.zero_n - n4 * 4) p.zero_out[n4 * 4 + threadIdx.x] = 0.f;
+  }
   TileMap t;
   if (!map_tile<MODE, BMA>(p, t)) return;
   const int tid = threadIdx.x;
@@ -1015,7 +1023,8 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
 hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_weights& w,
                              const void* x, const int32_t* offsets, const int32_t* perm_token,
                              const float* perm_w, float* y_perm, float* y, void* H,
-                             hipStream_t st, hipEvent_t ev_mid, const float* shared_w) {
+                             hipStream_t st, hipEvent_t ev_mid, const float* shared_w,
+                             bool zero_y) {
   if (s.kind == MOE_EXPERT_LINEAR_BIAS) {
     const int64_t n = L.P_max * s.d;
     const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
@@ -1056,7 +1065,11 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.tail_cap = tail_cap;
   g.group_n = 8;  // weight tiles per expert-aligned block of the tile order
 
-  // gate / up
+  // gate / up (it also clears y for the atomic combine when asked)
+  if (zero_y && y) {
+    g.zero_out = y;
+    g.zero_n = s.T * (int64_t)s.d;
+  }
   g.A = (const uint16_t*)x;
   g.A_bytes = s.T * (int64_t)s.d * 2;
   g.B0 = w.W1; g.B1 = w.W3; g.B0s = w.W1s; g.B1s = w.W3s;
@@ -1086,6 +1099,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
 
   // down (+ combine)
   GemmParams g2 = g;
+  g2.zero_out = nullptr;
+  g2.zero_n = 0;
   g2.A = (const uint16_t*)H;
   g2.A_bytes = L.H_rows * (int64_t)s.d_ff * 2;
   g2.B0 = w.W2; g2.B1 = nullptr; g2.B0s = w.W2s; g2.B1s = nullptr;

@@ -129,7 +129,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L,
                              const int32_t* offsets, const int32_t* perm_token,
                              const float* perm_w, float* y_perm, float* y,
                              void* H, hipStream_t st, hipEvent_t ev_mid = nullptr,
-                             const float* shared_w = nullptr);
+                             const float* shared_w = nullptr, bool zero_y = false);
 
 // y_perm holds P_max grouped rows, then (with a shared expert) T rows of
 // the shared expert's output.

@@ -823,19 +823,19 @@ __global__ __launch_bounds__(256) void linear_bias_kernel(
 // p.tail_slab (GATEUP: [row][128 gate | 128 up] sums, already scaled;
 // DOWN_PERM: [row][256 outputs]); sum them in piece order and finish the
 // tile's valid rows (GATEUP: SwiGLU into H; DOWN_PERM: the grouped output).
-// kFixBands workgroups share a tile, one band of rows each: workgroup b is
-// XCD b % 8, then (tail tile, band) of b / 8 (the same schedule arithmetic
-// as the GEMM, from the same offsets).
+// One workgroup per band of 16 rows (BM / 16 bands per tile, at most
+// kFixBands): workgroup b is XCD b % 8, then (tail tile, band) of b / 8 (the
+// same schedule arithmetic as the GEMM, from the same offsets).
 constexpr int kFixBands = 16;
 template <int MODE, int BM>
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   constexpr int ROWS = DMA_BM / kFixBands;  // rows per band (16)
   __shared__ int s_scan[4];
   __shared__ int s_pre[kMaxSegments + 1];
+  constexpr int NB = BM / ROWS < kFixBands ? BM / ROWS : kFixBands;  // bands of a tile
   const int xcd = (int)(blockIdx.x % kNumXcd);
-  const int r = (int)(blockIdx.x / kNumXcd / kFixBands);
-  const int band = (int)(blockIdx.x / kNumXcd % kFixBands);
-  if (band * ROWS >= BM) return;  // tiles of BM < 256 rows have fewer bands
+  const int r = (int)(blockIdx.x / kNumXcd / NB);
+  const int band = (int)(blockIdx.x / kNumXcd % NB);
   const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
   int64_t qtail = 0;
   int rem = 0, S = 1;
@@ -986,7 +986,11 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   p.mt_max = (int)((p.P_max + BMA - 1) / BMA + p.E + (p.has_shared ? (p.T + BMA - 1) / BMA : 0));
   grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA><<<sched_grid(p), 256, C::LDS, st>>>(p);
   if (slab_mode && p.split_max > 1)
-    tail_fixup_kernel<MODE, BMA><<<(unsigned)(kNumXcd * slots * kFixBands), 256, 0, st>>>(p);
+    // split tail tiles exist only with S >= 2 pieces, so rem <= slots / 2 of
+    // them per XCD; bands past BMA rows hold nothing
+    tail_fixup_kernel<MODE, BMA><<<(unsigned)(kNumXcd * std::max(1, slots / 2) *
+                                              std::min(kFixBands, BMA / (DMA_BM / kFixBands))),
+                                   256, 0, st>>>(p);
   return hipGetLastError();
 }
 

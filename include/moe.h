@@ -101,6 +101,18 @@ typedef enum moe_overflow {
                                Q2, DeepSeek-V3's choice; "MoE 并行" Q4); needs has_shared */
 } moe_overflow;
 
+/* Form of the combine inside moe_forward. */
+typedef enum moe_combine_form {
+  MOE_COMBINE_AUTO = 0,    /* chosen from the shape: FUSED when experts average 32 rows or
+                              fewer (decode-sized batches), else GROUPED */
+  MOE_COMBINE_GROUPED = 1, /* the down projection writes a grouped fp32 output in the
+                              workspace; a combine pass sums each token's rows in slot order
+                              (no read-modify-write of y; bit-deterministic) */
+  MOE_COMBINE_FUSED = 2    /* the combine is fused into the down projection's epilogue as
+                              fp32 atomic adds into a cleared y (the weighted scatter-add;
+                              summation order not fixed) */
+} moe_combine_form;
+
 /* The problem's parameters (fde-learning "MoE 并行" 关键参数: num_experts, top_k,
  * expert_capacity; tutorial §4.1 MoELayer(d_model, num_experts, top_k)). */
 typedef struct moe_shape {
@@ -122,6 +134,8 @@ typedef struct moe_shape {
                           (2..64, dividing E); 0 or 1 = off */
   int32_t topk_groups; /* groups a token may use, 1..n_groups, with
                           top_k <= topk_groups * E / n_groups */
+  int32_t combine;     /* moe_combine_form of moe_forward; 0 (auto) when zero-initialised.
+                          Part of the shape, so moe_workspace_bytes accounts for it */
 } moe_shape;
 
 /* Expert weights [device].  Unused members may be NULL. */
@@ -258,12 +272,11 @@ moe_status moe_combine(const moe_shape* shape, const float* y_perm,
  * moe_reroute describes; overflow to the shared expert as moe_combine does).
  * counts stays the router's loads before capacity; offsets are those of the
  * final grouping.
- * With few rows per expert (P_max / E <= 32, decode-sized batches) the
- * combine is fused into the down projection as fp32 atomic adds into a
- * cleared y, so that projection can split K over workgroups; otherwise the
- * down projection writes a grouped fp32 output in the workspace and a
- * combine pass sums each token's rows in slot order (no read-modify-write of
- * y, and a deterministic result).  y [device] fp32 [T, d] is overwritten.  topk_idx, topk_w,
+ * shape->combine picks the combine's form (moe_combine_form): fused into the
+ * down projection as fp32 atomic adds into a cleared y, or a grouped fp32
+ * output in the workspace summed by a combine pass in slot order (no
+ * read-modify-write of y, and a deterministic result).  AUTO fuses it when
+ * experts average 32 rows or fewer (P_max / E <= 32, decode-sized batches).  y [device] fp32 [T, d] is overwritten.  topk_idx, topk_w,
  * counts, offsets [device] are outputs as above; ws [device] holds
  * moe_workspace_bytes(shape) bytes.  No host synchronisation. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g,

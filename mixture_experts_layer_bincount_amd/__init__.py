@@ -26,6 +26,8 @@ DT_F32, DT_BF16, DT_FP8_E4M3, DT_INT8, DT_INT4 = 0, 1, 2, 3, 4
 LINEAR_BIAS, SWIGLU = 0, 1
 OVERFLOW_DROP, OVERFLOW_REROUTE, OVERFLOW_SHARED = 0, 1, 2
 OVERFLOW = {"drop": OVERFLOW_DROP, "reroute": OVERFLOW_REROUTE, "shared": OVERFLOW_SHARED}
+COMBINE_AUTO, COMBINE_GROUPED, COMBINE_FUSED = 0, 1, 2
+COMBINE = {"auto": COMBINE_AUTO, "grouped": COMBINE_GROUPED, "fused": COMBINE_FUSED}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_from_logits",
@@ -48,7 +50,7 @@ class Shape(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("has_shared", ctypes.c_int32), ("overflow", ctypes.c_int32),
                 ("reroute_rounds", ctypes.c_int32), ("n_groups", ctypes.c_int32),
-                ("topk_groups", ctypes.c_int32)]
+                ("topk_groups", ctypes.c_int32), ("combine", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -120,14 +122,17 @@ def _check(st):
 
 def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=DT_BF16,
                kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0,
-               n_groups=0, topk_groups=0) -> Shape:
+               n_groups=0, topk_groups=0, combine=COMBINE_AUTO) -> Shape:
     """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared").
-    n_groups / topk_groups: group-limited routing (0 = off)."""
+    n_groups / topk_groups: group-limited routing (0 = off).
+    combine: COMBINE_* or its name ("auto", "grouped", "fused")."""
     if isinstance(overflow, str):
         overflow = OVERFLOW[overflow]
+    if isinstance(combine, str):
+        combine = COMBINE[combine]
     return Shape(int(T), int(d), int(E), int(top_k), int(d_ff), int(capacity), int(act_dtype),
                  int(w_dtype), int(kind), int(bool(has_shared)), int(overflow),
-                 int(reroute_rounds), int(n_groups), int(topk_groups))
+                 int(reroute_rounds), int(n_groups), int(topk_groups), int(combine))
 
 
 def make_weights(**tensors) -> Weights:

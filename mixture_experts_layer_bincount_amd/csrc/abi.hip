@@ -52,6 +52,8 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     return fail(MOE_ERR_INVALID, "reroute_rounds=%d must be in [0, 1024]", s->reroute_rounds);
   if (s->overflow == MOE_OVERFLOW_SHARED && !s->has_shared)
     return fail(MOE_ERR_INVALID, "overflow to the shared expert needs has_shared");
+  if (s->combine < MOE_COMBINE_AUTO || s->combine > MOE_COMBINE_FUSED)
+    return fail(MOE_ERR_INVALID, "combine=%d is not a moe_combine_form", s->combine);
   if (s->n_groups < 0 || s->n_groups > 64)
     return fail(MOE_ERR_INVALID, "n_groups=%d must be in [0, 64]", s->n_groups);
   if (s->n_groups > 1) {
@@ -231,19 +233,11 @@ WsLayout ws_layout(const moe_shape& s) {
   off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
   L.off_H = off;
   if (s.kind == MOE_EXPERT_SWIGLU) off = align256(off + (size_t)L.H_rows * s.d_ff * 2);
-  // partial tiles of split tail tiles of the grouped-output down projection:
-  // one per workgroup slot of the device (one workgroup per CU)
-  L.tail_cap = 0;
+  // partial tiles of split tail tiles (gate/up with a long K, the grouped-
+  // output down projection with a long K)
+  L.slab_floats = gemm_slab_floats(s, L.P_max);
   L.off_slab = off;
-  if (s.kind == MOE_EXPERT_SWIGLU) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    L.tail_cap = std::max(cus, 256);
-    off = align256(off + (size_t)L.tail_cap * 65536 * sizeof(float));
-  }
+  off = align256(off + L.slab_floats * sizeof(float));
   L.grouped_combine = use_grouped_combine(s);
   L.off_Yp = off;
   if (L.grouped_combine) off = align256(off + (size_t)L.H_rows * s.d * sizeof(float));
@@ -272,14 +266,11 @@ WsLayout ws_layout(const moe_shape& s) {
 }
 
 bool use_grouped_combine(const moe_shape& s) {
-  if (s.kind != MOE_EXPERT_SWIGLU) return false;
-  const char* v = getenv("MOE_COMBINE");  // "grouped" | "atomic" (comparison)
-  if (v && !strcmp(v, "grouped")) return true;
-  if (v && !strcmp(v, "atomic")) return false;
+  if (s.combine == MOE_COMBINE_GROUPED) return true;
+  if (s.combine == MOE_COMBINE_FUSED || s.kind != MOE_EXPERT_SWIGLU) return false;
   // Few rows per expert (decode): the atomic form, whose down projection may
   // split K over workgroups; otherwise the grouped output (measured faster
-  // with many experts per token or a large y, equal at the Mixtral shape, and
-  // deterministic).
+  // with many experts per token or a large y, and deterministic).
   const int64_t A = s.T * (int64_t)s.top_k;
   const int64_t P_max = (s.capacity < 0) ? A : std::min<int64_t>(A, (int64_t)s.E * s.capacity);
   return P_max / s.E > 32;

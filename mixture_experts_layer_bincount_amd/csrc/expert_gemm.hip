@@ -46,6 +46,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -91,8 +93,9 @@ struct GemmParams {
   int split_max;              // K ranges a tail tile may be cut into (1: none)
   int kunit;                  // K steps of BK per unit of the schedule
   int slots;                  // workgroups one XCD runs at once
-  float* tail_slab;           // MODE_DOWN_PERM: fp32 partial tiles of split tail tiles
-  int tail_cap;               //   (room for tail_cap tiles of 64 Ki floats)
+  float* tail_slab;           // fp32 partial tiles of split tail tiles (GATEUP, DOWN_PERM)
+  int64_t slab_floats;        //   its size in floats
+  int slab_piece;             //   floats per partial tile: activation-tile rows x 256
   int group_n;                // weight tiles per expert-aligned block of the tile order
   int krot;                   // K walk start of workgroup b: (b * krot) mod (its K steps); 0 = none
   float* zero_out;            // zero_n floats (16-byte aligned) the workgroups clear first, or NULL
@@ -273,7 +276,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
             su = t.shared_e ? p.sc1s[gi] : p.sc1[(int64_t)t.e * (N / kFp8Group) + gi];
           }
           if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
-            float* sl = p.tail_slab + (int64_t)t.slab * 65536 + (int64_t)(m - t.m0) * 256 + (n - n0);
+            float* sl = p.tail_slab + (int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0);
             *(float4*)sl = make_float4(
                 (acc[i][j][q * 4] - cr) * sg, (acc[i][j][q * 4 + 1] - cr) * sg,
                 (acc[i][j][q * 4 + 2] - cr) * sg, (acc[i][j][q * 4 + 3] - cr) * sg);
@@ -333,8 +336,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
             if (MODE == MODE_DOWN)
               atomicAdd(&p.y[orow * N + n], wgt * v);
             else if (t.slab >= 0)  // piece of a split tail tile: its partial tile
-              p.tail_slab[(int64_t)t.slab * 65536 +
-                          (int64_t)(m - t.m0) * (65536 / BMT) + (n - n0)] = v;
+              p.tail_slab[(int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0)] = v;
             else
               p.y_perm[orow * N + n] = v;
           }
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   TileMap t;
   tile_place<BM>(p, s_pre, qtail + r, t);
   if (band * ROWS >= t.rows - t.m0) return;  // the band holds no rows of the segment
-  const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * 65536;
+  const float* slab = p.tail_slab + (int64_t)(xcd * p.slots + r * S) * p.slab_piece;
   const int64_t obase = (t.shared_e ? p.P_max : (int64_t)t.seg) + t.m0;
   // ROWS x 256 floats per band: 16 rows x 64 float4 = 4 float4 per thread;
   // GATEUP pairs the gate float4 at column c with the up float4 at c + 128
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
   for (int pc = 1; pc < S; ++pc) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const float* src = slab + (int64_t)pc * 65536 + row[v] * 256 + col[v];
+      const float* src = slab + (int64_t)pc * p.slab_piece + row[v] * 256 + col[v];
       const float4 b = *(const float4*)src;
       a[v].x += b.x; a[v].y += b.y; a[v].z += b.z; a[v].w += b.w;
       if (MODE == MODE_GATEUP) {
@@ -942,16 +944,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Workgroups one XCD runs at once for a kernel of 256 threads and `lds`
-// bytes of LDS (after its LDS opt-in).
-int xcd_slots(const void* kernel, size_t lds) {
-  int dev = 0, cus = 0, occ = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+// bytes of LDS (after its LDS opt-in) on device `dev`.
+int xcd_slots(const void* kernel, size_t lds, int dev) {
+  int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, lds) != hipSuccess)
     occ = 1;
-  return std::max(1, cus / kNumXcd) * std::max(1, occ);
+  return std::max(1, device_cus(dev) / kNumXcd) * std::max(1, occ);
 }
+
+// Per-device launch facts of one kernel instantiation (its LDS opt-in and
+// the workgroups an XCD runs at once), set up once per device.
+struct KernelSlots {
+  std::once_flag once[kMaxDevices];
+  hipError_t err[kMaxDevices] = {};
+  int slots[kMaxDevices] = {};
+};
 
 // Grid of the tile schedule: kNumXcd x the bound of any XCD's units.
 inline unsigned sched_grid(const GemmParams& p) {
@@ -970,18 +977,24 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
   using C = DmaCfg<KB, NS, wq_bits(WQ), BMA>;
   const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA>;
-  static int slots = 0;
-  if (!slots) {
-    hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)C::LDS);
-    if (err != hipSuccess) return err;
-    slots = xcd_slots(kern, C::LDS);
-  }
+  static KernelSlots ks;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(ks.once[dev], [&] {
+    ks.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+    if (ks.err[dev] == hipSuccess) ks.slots[dev] = xcd_slots(kern, C::LDS, dev);
+  });
+  if (ks.err[dev] != hipSuccess) return ks.err[dev];
+  const int slots = ks.slots[dev];
   GemmParams p = p0;
   p.kunit = KB / BK;
   p.slots = slots;
+  p.slab_piece = BMA * 256;
   constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
-  if (slab_mode && (!p.tail_slab || kNumXcd * slots > p.tail_cap)) p.split_max = 1;
+  if (slab_mode && (!p.tail_slab || (int64_t)kNumXcd * slots * p.slab_piece > p.slab_floats))
+    p.split_max = 1;
   // row tiles of BMA rows: sum_e ceil(rows_e / BMA) <= P_max / BMA + E (+ shared)
   p.mt_max = (int)((p.P_max + BMA - 1) / BMA + p.E + (p.has_shared ? (p.T + BMA - 1) / BMA : 0));
   grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA><<<sched_grid(p), 256, C::LDS, st>>>(p);
@@ -1024,6 +1037,42 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
 
 }  // namespace
 
+int device_cus(int dev) {
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(once[dev], [&] {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                n > 0)
+                   ? n
+                   : 256;
+  });
+  return cus[dev];
+}
+
+int current_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  return device_cus(dev);
+}
+
+size_t gemm_slab_floats(const moe_shape& s, int64_t P_max) {
+  if (s.kind != MOE_EXPERT_SWIGLU || s.E <= 0) return 0;
+  // the launches that may split tail tiles through the slab: gate/up for
+  // d >= 4096, the grouped-output down projection for d_ff >= 4096
+  if (s.d < 4096 && s.d_ff < 4096) return 0;
+  const int64_t rows_avg = P_max / s.E;
+  // activation-tile rows and workgroups per CU of launch_gemm's choice
+  int bma = 256, per_cu = 1;
+  if (rows_avg <= 32) {
+    bma = (s.w_dtype == MOE_DT_BF16 && rows_avg <= 16) ? 32 : 64;
+    per_cu = 2;
+  }
+  const int cus = current_device_cus();
+  return (size_t)kNumXcd * std::max(1, cus / kNumXcd) * per_cu * bma * 256;
+}
+
 hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_weights& w,
                              const void* x, const int32_t* offsets, const int32_t* perm_token,
                              const float* perm_w, float* y_perm, float* y, void* H,
@@ -1050,8 +1099,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
                  : s.w_dtype == MOE_DT_INT4   ? WQ_INT4
                                               : WQ_BF16;
   const int has_sh = s.has_shared ? 1 : 0;
-  float* tail_slab = H ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
-  const int tail_cap = L.tail_cap;
+  float* tail_slab = (H && L.slab_floats) ? (float*)((char*)H + (L.off_slab - L.off_H)) : nullptr;
   // Upper bound of row tiles: sum_e ceil(rows_e / BM) <= P_max / BM + E (+ shared).
   constexpr int BM = DMA_BM;
   const int64_t mt_bound = (L.P_max + BM - 1) / BM + s.E + (has_sh ? (s.T + BM - 1) / BM : 0);
@@ -1066,7 +1114,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.has_shared = has_sh;
   g.mt_max = (int)mt_bound;
   g.tail_slab = tail_slab;
-  g.tail_cap = tail_cap;
+  g.slab_floats = L.slab_floats;
   g.group_n = 8;  // weight tiles per expert-aligned block of the tile order
 
   // gate / up (it also clears y for the atomic combine when asked)
@@ -1125,7 +1173,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // at d_ff = 1408 and 2048, a gain at 14336).
   g2.split_max = (y || s.d_ff >= 4096) ? std::max(1, s.d_ff / BK / 8) : 1;
   g2.tail_slab = tail_slab;
-  g2.tail_cap = tail_cap;
+  g2.slab_floats = L.slab_floats;
   if (y)
     return launch_gemm<MODE_DOWN>(wq, rows_avg, g2, st);
   return launch_gemm<MODE_DOWN_PERM>(wq, rows_avg, g2, st);

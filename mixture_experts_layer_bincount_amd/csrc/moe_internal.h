@@ -26,6 +26,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+constexpr int kMaxDevices = 64;  // devices whose launch facts are cached
+
+// Compute units of device `dev` (of the current device), queried once per device.
+int device_cus(int dev);
+int current_device_cus();
+
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
   int router_splits;     // split-K factor of the router GEMM
@@ -40,8 +46,8 @@ struct WsLayout {
   size_t off_perm_w;     // fp32  [P_max]
   size_t off_slot_pos;   // int32 [T*k]
   size_t off_H;          // bf16  [H_rows, d_ff]
-  int tail_cap;          // partial tiles the tail slab holds
-  size_t off_slab;       // fp32  [tail_cap, 65536] split tail tiles (SwiGLU)
+  size_t slab_floats;    // floats of the tail slab (0: no tail tile is split)
+  size_t off_slab;       // fp32  [slab_floats] partial tiles of split tail tiles (SwiGLU)
   bool grouped_combine;  // moe_forward: grouped output + combine instead of atomics
   size_t off_Yp;         // fp32  [H_rows, d] (grouped_combine only)
   // overflow re-routing (always carved; small unless many rounds)
@@ -72,6 +78,11 @@ int reroute_rounds_eff(const moe_shape& s);
 int reroute_candidates(const moe_shape& s);
 
 WsLayout ws_layout(const moe_shape& s);
+
+// Floats of the partial-tile slab the grouped GEMMs may split tail tiles
+// through for this shape (0 when neither launch splits): one partial tile
+// per workgroup slot of the device, sized to the activation tile.
+size_t gemm_slab_floats(const moe_shape& s, int64_t P_max);
 
 // Whether moe_forward combines through a grouped fp32 output and a combine
 // kernel (deterministic, no read-modify-write of y) rather than atomics in

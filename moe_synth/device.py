@@ -19,9 +19,10 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def upload(wl: Workload, device="cuda", workers=None):
+def upload(wl: Workload, device="cuda", workers=None, keep_host=None):
     """Returns dict(x, W_g, b_g, weights) of device tensors; expert weights
-    are stacked [E, out, in] (and scales [E, out/128])."""
+    are stacked [E, out, in] (and scales [E, out/128]).  keep_host: a dict
+    that receives each routed expert's host arrays (e -> dict), or None."""
     c = wl._wcfg
     dev = torch.device(device)
     out = {"x": to_device(wl.x(), dev), "W_g": to_device(wl.W_g(), dev)}
@@ -34,6 +35,8 @@ def upload(wl: Workload, device="cuda", workers=None):
             w = wl.expert(e)
             Ws.append(w["W"])
             bs.append(w["b"])
+            if keep_host is not None:
+                keep_host[e] = w
         weights["W"] = to_device(np.stack(Ws), dev)
         weights["b"] = to_device(np.stack(bs), dev)
     else:
@@ -45,6 +48,8 @@ def upload(wl: Workload, device="cuda", workers=None):
         def put(e, w):
             for name, a in w.items():
                 weights[name][e].copy_(to_device(a, "cpu"), non_blocking=False)
+            if keep_host is not None:
+                keep_host[e] = w
 
         wl.experts_parallel(range(c.E), put, workers=workers)
         sh = wl.shared()

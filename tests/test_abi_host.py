@@ -84,10 +84,12 @@ def test_workspace_bytes_degenerate(moe, T, d, E, k):
     (dict(overflow=2), "has_shared"), (dict(n_groups=3, topk_groups=1), "divide"),
     (dict(n_groups=4, topk_groups=0), "topk_groups"), (dict(n_groups=4, topk_groups=5), "topk_groups"),
     (dict(n_groups=8, topk_groups=1, top_k=2), "top_k"), (dict(n_groups=65, topk_groups=1), "n_groups"),
-    (dict(n_groups=4, topk_groups=2, overflow=1, capacity=4), "re-routing")])
+    (dict(n_groups=4, topk_groups=2, overflow=1, capacity=4), "re-routing"),
+    (dict(combine=3), "combine="), (dict(combine=-1), "combine=")])
 def test_validation_rejects_bad_shapes(moe, kw, needle):
     base = dict(T=16, d=256, E=8, top_k=2, d_ff=128, capacity=-1, act_dtype=1, w_dtype=1,
-                kind=1, has_shared=False, overflow=0, reroute_rounds=0, n_groups=0, topk_groups=0)
+                kind=1, has_shared=False, overflow=0, reroute_rounds=0, n_groups=0, topk_groups=0,
+                combine=0)
     base.update(kw)
     s = moe.make_shape(**base)
     fake = 256  # never dereferenced: validation fails first
@@ -129,6 +131,19 @@ def test_validation_null_and_alignment(moe):
     with pytest.raises(moe.MoEError, match="shared"):
         moe.moe_forward(moe.make_shape(16, 8, 4, 2, 0, -1, 0, 0, 0, True), 256, 256, None,
                         moe.make_weights(W=256, b=256), 256, 256, 256, 256, 256, 256, stream=0)
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_workspace_follows_the_combine_form(moe, T):
+    """The combine form is part of the shape: the grouped form reserves the
+    grouped fp32 output (P_max rows of d floats) that the fused form does
+    not, and the byte count is a function of the shape alone."""
+    fused = moe.moe_workspace_bytes(moe.make_shape(T, 4096, 8, 2, 14336, combine="fused"))
+    grouped = moe.moe_workspace_bytes(moe.make_shape(T, 4096, 8, 2, 14336, combine="grouped"))
+    auto = moe.moe_workspace_bytes(moe.make_shape(T, 4096, 8, 2, 14336))
+    assert grouped >= fused + T * 2 * 4096 * 4
+    assert auto == (fused if T * 2 // 8 <= 32 else grouped)
+    assert fused == moe.moe_workspace_bytes(moe.make_shape(T, 4096, 8, 2, 14336, combine="fused"))
 
 
 def test_workspace_covers_rerouting(moe):

@@ -27,3 +27,25 @@ def test_workloads_named_in_the_bench_exist():
         c = CONFIGS[name]
         assert (c.T, c.d, c.E, c.k, c.d_ff) == (64, 4096, 8, 2, 14336)
         assert c.w_from == "mixtral" and c.x_from == "mixtral"
+
+
+def test_roofline_floors_of_the_workloads():
+    """The binding floors bench.py reports against: the Mixtral-shaped layer's
+    2.886e12 expert FLOPs at 2.5 PFLOP/s (1.155 ms, MFMA-bound); the
+    fine-grained layer's 257 experts' bf16 weights (22.64 GB) at 8 TB/s
+    (2.83 ms, HBM-bound) against 1.30 ms of MFMA time; the same in fp8 codes
+    with their scales (11.32 GB, 1.42 ms)."""
+    import bench
+    from moe_synth.configs import CONFIGS
+    f = bench.roofline_floor(CONFIGS["mixtral"], [1024] * 8, 8192)
+    assert f["bound"] == "mfma" and abs(f["floor_ms"] - 1.1545) < 1e-3
+    assert f["touched_experts"] == 8
+    f = bench.roofline_floor(CONFIGS["fine_grained"], [128] * 256, 32768)
+    assert f["bound"] == "hbm" and abs(f["mfma_floor_ms"] - 1.2984) < 1e-3
+    assert abs(bench.weight_bytes(CONFIGS["fine_grained"], 257) - 22.64e9) < 0.01e9
+    assert 2.83 < f["hbm_floor_ms"] < 2.86
+    f8 = bench.roofline_floor(CONFIGS["fine_grained_fp8"], [128] * 256, 32768)
+    assert 1.41 < f8["hbm_floor_ms"] < 1.45 and f8["bound"] == "hbm"
+    # an expert the step never touched costs no weight bytes
+    f = bench.roofline_floor(CONFIGS["capacity_skew"], [640] * 30 + [0] * 34, 640 * 30)
+    assert f["touched_experts"] == 30

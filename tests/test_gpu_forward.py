@@ -3,14 +3,18 @@
 Small shapes are compared on every output element; they span several tiles in
 every GEMM dimension with ragged row tails.  The named workloads run at full
 size, in the launch configuration the benchmark times, and are compared on
-sampled tokens that the oracle evaluates one by one.
+every token as well: the oracle's loop over experts is fed each expert's
+weights decoded ahead on a thread pool (ExpertStream), so it does not wait
+for input generation.
 """
 import numpy as np
 import pytest
 
 import oracle
 from moe_synth import Workload, custom_config, get_config
-from tests.parity import check_forward, gpu_forward, gpu_logits, rel_err
+from moe_synth.gen import INT4X2
+from tests.parity import (ExpertStream, check_forward, expert_bytes_f64, gpu_forward, gpu_logits,
+                          rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,14 +107,13 @@ def test_tiny_page_layer(moe):
 
 
 @pytest.mark.parametrize("T,seed,shared", [(600, 5, False), (64, 6, False), (200, 7, True)])
-def test_unfused_path_matches_fused(moe, monkeypatch, T, seed, shared):
+def test_unfused_path_matches_fused(moe, T, seed, shared):
     """moe_expert_ffn into a grouped output, then moe_combine, against the
     fused scatter-add path and the oracle (600 tokens; 64, a few rows per
     expert; 200 with a shared expert, whose rows follow the grouped rows)."""
-    monkeypatch.setenv("MOE_COMBINE", "atomic")
     cfg = custom_config(T, 256, 8, 2, 256, cf=1.0, seed=seed, shared=shared)
     wl = Workload(cfg)
-    out, layer, dev = gpu_forward(wl)
+    out, layer, dev = gpu_forward(wl, combine="fused")
     s = layer.shape
     ws = moe.workspace(s)
     T, k, d = cfg.T, cfg.k, cfg.d
@@ -138,27 +141,25 @@ def test_unfused_path_matches_fused(moe, monkeypatch, T, seed, shared):
     check_forward(wl, out2)
 
 
-@pytest.mark.parametrize("form", ["atomic", "grouped"])
-def test_combine_forms(moe, monkeypatch, form):
+@pytest.mark.parametrize("form", ["fused", "grouped"])
+def test_combine_forms(moe, form):
     """Both combine forms of moe_forward against the oracle: fp32 atomic adds
     in the down projection (the default at decode sizes), and a grouped
     output summed by the combine pass, on a shape with k = 4, a shared expert
     and a capacity limit."""
-    monkeypatch.setenv("MOE_COMBINE", form)
     cfg = custom_config(400, 256, 16, 4, 256, shared=True, cf=1.25, seed=41)
     wl = Workload(cfg)
-    out, _, _ = gpu_forward(wl)
+    out, _, _ = gpu_forward(wl, combine=form)
     rep = check_forward(wl, out)
     print(f"[combine {form}] err={rep['err']:.3e}", flush=True)
 
 
-def test_grouped_combine_is_deterministic(moe, monkeypatch):
+def test_grouped_combine_is_deterministic(moe):
     """The grouped-output combine sums in slot order: two runs are bit-equal
     even with k = 8 and a shared expert."""
-    monkeypatch.setenv("MOE_COMBINE", "grouped")
     cfg = custom_config(300, 256, 32, 8, 128, shared=True, seed=43)
     wl = Workload(cfg)
-    out1, layer, dev = gpu_forward(wl)
+    out1, layer, dev = gpu_forward(wl, combine="grouped")
     layer(dev["x"])
     torch.cuda.synchronize()
     assert np.array_equal(layer.y.cpu().numpy(), out1["y"])
@@ -188,25 +189,69 @@ def test_determinism_k2(moe):
     assert np.array_equal(layer.y.cpu().numpy(), out1["y"])
 
 
-def _sample_tokens(T, n, seed):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    s.update({0, T - 1})
-    return np.array(sorted(s))
+def _full_size(wl, **kw):
+    """moe_forward at full size, then the oracle on every token, fed from the
+    host copies of the uploaded weights."""
+    host = {}
+    out, layer, dev = gpu_forward(wl, keep_host=host, **kw)
+    stream = ExpertStream(lambda e: host[e], wl.cfg.E, expert_bytes_f64(wl.cfg))
+    return out, layer, dev, stream
 
 
-@pytest.mark.parametrize("name,nsample", [("mixtral", 40), ("decode", 64),
-                                          ("capacity_skew", 40), ("fine_grained", 12),
-                                          ("fine_grained_fp8", 12), ("fine_grained_int8", 12),
-                                          ("fine_grained_int4", 12), ("decode_int4", 64),
-                                          ("decode_fp8", 64), ("decode_int8", 64)])
-def test_workload_full_size(moe, name, nsample):
+@pytest.mark.parametrize("name", ["mixtral", "decode", "capacity_skew", "fine_grained",
+                                  "fine_grained_fp8", "fine_grained_int8", "fine_grained_int4",
+                                  "decode_int4", "decode_fp8", "decode_int8"])
+def test_workload_full_size(moe, name):
+    """Every token of the named workload against the oracle.  The fine-grained
+    layer's 256 experts each hold about 128 rows, so every expert segment and
+    every 256-row tile of the shared expert is compared."""
     print(f"[workload] {name}", flush=True)
     wl = Workload(get_config(name))
+    out, _, _, stream = _full_size(wl)
+    try:
+        rep = check_forward(wl, out, experts=stream)
+    finally:
+        stream.close()
+    print(f"  err={rep['err']:.3e} (nonzero rows {rep['nonzero_rows']}: "
+          f"{rep['err_nonzero_rows']:.3e}) tokens={rep['tokens']} flipped={rep['flipped']} "
+          f"kept={rep['kept']}", flush=True)
+    assert rep["tokens"] == wl.cfg.T
+
+
+class _Int4WithMinus8(Workload):
+    """The synthetic int4 weights with about 6% of the codes set to -8 (nibble
+    0), which the format accepts but the quantiser never writes."""
+
+    def _poke(self, w, seed):
+        rng = np.random.default_rng(seed)
+        for n in ("W1", "W3", "W2"):
+            a = np.ascontiguousarray(w[n]).view(np.uint8).copy()
+            lo = rng.random(a.shape) < 0.06
+            hi = rng.random(a.shape) < 0.06
+            a[lo] &= 0xF0
+            a[hi] &= 0x0F
+            w[n] = a.view(INT4X2)
+        return w
+
+    def expert(self, e):
+        return self._poke(super().expert(e), 1000 + e)
+
+    def shared(self):
+        w = super().shared()
+        return None if w is None else self._poke(w, 999)
+
+
+@pytest.mark.parametrize("T,d,E,k,d_ff,shared", [(700, 512, 8, 2, 384, True),
+                                                  (64, 512, 8, 2, 1408, False),
+                                                  (300, 4096, 4, 2, 256, False)])
+def test_int4_code_minus8(moe, T, d, E, k, d_ff, shared):
+    cfg = custom_config(T, d, E, k, d_ff, w="int4", shared=shared, seed=T + 17)
+    wl = _Int4WithMinus8(cfg)
+    w0 = np.ascontiguousarray(wl.expert(0)["W1"]).view(np.uint8)
+    assert ((w0 & 0x0F) == 0).any() and ((w0 >> 4) == 0).any()
     out, _, _ = gpu_forward(wl)
-    toks = None if nsample >= wl.cfg.T else _sample_tokens(wl.cfg.T, nsample, seed=1)
-    rep = check_forward(wl, out, tokens=toks)
-    print(f"  err={rep['err']:.3e} flipped={rep['flipped']} kept={rep['kept']}", flush=True)
+    rep = check_forward(wl, out)
+    print(f"[int4 -8] T={T} d={d} err={rep['err']:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("T,d,E,k,d_ff,cf,shared,w,G,M", [
@@ -233,9 +278,12 @@ def test_fine_grained_group_limited_full_size(moe):
     experts and at most 4 groups per token, at full size."""
     print("[workload] fine_grained, 8 groups, top-4 groups", flush=True)
     wl = Workload(get_config("fine_grained"))
-    out, layer, dev = gpu_forward(wl, groups=8, topk_groups=4)
+    out, layer, dev, stream = _full_size(wl, groups=8, topk_groups=4)
     gl = gpu_logits(layer, dev)
-    rep = check_forward(wl, out, tokens=_sample_tokens(wl.cfg.T, 12, seed=3), decide_on=gl,
-                        groups=8, topk_groups=4)
+    try:
+        rep = check_forward(wl, out, decide_on=gl, groups=8, topk_groups=4, experts=stream)
+    finally:
+        stream.close()
+    assert rep["tokens"] == wl.cfg.T
     print(f"  err={rep['err']:.3e} kept={rep['kept']}", flush=True)
 

@@ -17,6 +17,7 @@ import pytest
 import oracle
 from moe_synth import Workload, custom_config, get_config
 from tests.conftest import GOLDEN
+from tests.parity import ExpertStream, expert_bytes_f64
 from tests.parity import check_forward, gpu_forward, gpu_logits, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -128,23 +129,21 @@ FORWARD = [
     (777, 512, 16, 4, 128, 0.75, True, "bf16", "zipf1.5", "reroute", 2, "atomic"),
     (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5", "reroute", 3, None),
     (600, 256, 8, 2, 256, 1.0, True, "bf16", "zipf1.5", "shared", 0, "grouped"),
-    (600, 256, 8, 2, 256, 1.0, True, "bf16", "zipf1.5", "shared", 0, "atomic"),
+    (600, 256, 8, 2, 256, 1.0, True, "bf16", "zipf1.5", "shared", 0, "fused"),
     (64, 512, 8, 2, 1408, 0.5, True, "fp8_e4m3", "zipf1.5", "shared", 0, None),
     (300, 256, 4, 2, 256, None, True, "bf16", None, "shared", 0, None),   # nothing dropped
 ]
 
 
 @pytest.mark.parametrize("T,d,E,k,d_ff,cf,shared,w,bias,overflow,rounds,combine", FORWARD)
-def test_forward_overflow(moe, monkeypatch, T, d, E, k, d_ff, cf, shared, w, bias, overflow,
+def test_forward_overflow(moe, T, d, E, k, d_ff, cf, shared, w, bias, overflow,
                           rounds, combine):
     print(f"[forward {overflow}] T={T} d={d} E={E} k={k} d_ff={d_ff} cf={cf} shared={shared} "
           f"w={w} rounds={rounds} combine={combine}", flush=True)
-    if combine:
-        monkeypatch.setenv("MOE_COMBINE", combine)
     cfg = custom_config(T, d, E, k, d_ff, w=w, cf=cf, shared=shared, router_bias=bias,
                         seed=3 * T + d + E)
     wl = Workload(cfg)
-    out, layer, dev = gpu_forward(wl, overflow=overflow, rounds=rounds)
+    out, layer, dev = gpu_forward(wl, overflow=overflow, rounds=rounds, combine=combine or "auto")
     gl = gpu_logits(layer, dev)
     rep = check_forward(wl, out, overflow=overflow, rounds=rounds, decide_on=gl)
     # the policy matters here: the drop policy's result is measurably different
@@ -190,15 +189,22 @@ def test_staged_shared_overflow(moe):
         moe.moe_expert_ffn(s, layer.weights, dev["x"], offsets, perm_token, perm_w, None, y, ws)
 
 
-@pytest.mark.parametrize("rounds,nsample", [(1, 40), (4, 40)])
-def test_capacity_skew_rerouted_full_size(moe, rounds, nsample):
+@pytest.mark.parametrize("rounds", [1, 4])
+def test_capacity_skew_rerouted_full_size(moe, rounds):
     """The skewed workload (16384 tokens, 64 experts, C = 640) with its
-    overflow re-routed, in the launch configuration the benchmark times."""
+    overflow re-routed, in the launch configuration the benchmark times,
+    compared on every token."""
     print(f"[capacity_skew reroute] rounds={rounds}", flush=True)
     wl = Workload(get_config("capacity_skew"))
-    out, layer, dev = gpu_forward(wl, overflow="reroute", rounds=rounds)
+    host = {}
+    out, layer, dev = gpu_forward(wl, overflow="reroute", rounds=rounds, keep_host=host)
     gl = gpu_logits(layer, dev)
-    rng = np.random.default_rng(rounds)
-    toks = np.unique(np.concatenate([[0, wl.cfg.T - 1], rng.choice(wl.cfg.T, nsample, False)]))
-    rep = check_forward(wl, out, tokens=toks, overflow="reroute", rounds=rounds, decide_on=gl)
-    print(f"  err={rep['err']:.3e} kept={rep['kept']}", flush=True)
+    stream = ExpertStream(lambda e: host[e], wl.cfg.E, expert_bytes_f64(wl.cfg))
+    try:
+        rep = check_forward(wl, out, overflow="reroute", rounds=rounds, decide_on=gl,
+                            experts=stream)
+    finally:
+        stream.close()
+    assert rep["tokens"] == wl.cfg.T
+    print(f"  err={rep['err']:.3e} (nonzero rows {rep['err_nonzero_rows']:.3e}) "
+          f"kept={rep['kept']}", flush=True)

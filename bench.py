@@ -140,7 +140,7 @@ class Loaded:
                                   b_g=self.b_g, weights=dev_w, capacity=self.cap, kind=cfg.kind,
                                   w_dtype=cfg.w, has_shared=cfg.shared, overflow=overflow,
                                   reroute_rounds=rounds, n_groups=groups,
-                                  topk_groups=topk_groups)
+                                  topk_groups=topk_groups, hidden_split=cfg.hidden_split)
 
     def step(self):
         return self.layer(self.x)
@@ -273,7 +273,7 @@ def sub_record(name: str, steps: int, warmup: int, parity: bool) -> dict:
     floor = roofline_floor(c, kept_rows, kept)
     rec = {"config": {"T": c.T, "d": c.d, "E": c.E, "top_k": c.k, "d_ff": c.d_ff,
                       "expert": c.kind, "weights": c.w, "shared": c.shared,
-                      "capacity": L.cap},
+                      "capacity": L.cap, "hidden_split": c.hidden_split},
            "steps": steps, "ms_per_step": ms, "tokens_per_s": c.T / (ms * 1e-3),
            "kept_assignments": kept, **floor,
            "frac": floor["floor_ms"] / ms,

@@ -136,6 +136,13 @@ typedef struct moe_shape {
                           top_k <= topk_groups * E / n_groups */
   int32_t combine;     /* moe_combine_form of moe_forward; 0 (auto) when zero-initialised.
                           Part of the shape, so moe_workspace_bytes accounts for it */
+  int32_t hidden_split; /* SWIGLU: 0 = the hidden activation h = silu(x W1^T) * (x W3^T)
+                           is rounded to bf16 before the down projection (the usual bf16
+                           layer); 1 = compensated: h is kept as two bf16 terms, hi =
+                           bf16(h) and lo = bf16(h - hi), and the down projection sums
+                           both against W2 (h's rounding error about 2^-17 instead of
+                           2^-9; twice the down projection's MFMA work and hidden-buffer
+                           bytes) */
 } moe_shape;
 
 /* Expert weights [device].  Unused members may be NULL. */

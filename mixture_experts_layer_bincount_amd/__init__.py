@@ -50,7 +50,8 @@ class Shape(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32), ("kind", ctypes.c_int32),
                 ("has_shared", ctypes.c_int32), ("overflow", ctypes.c_int32),
                 ("reroute_rounds", ctypes.c_int32), ("n_groups", ctypes.c_int32),
-                ("topk_groups", ctypes.c_int32), ("combine", ctypes.c_int32)]
+                ("topk_groups", ctypes.c_int32), ("combine", ctypes.c_int32),
+                ("hidden_split", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -122,17 +123,19 @@ def _check(st):
 
 def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=DT_BF16,
                kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0,
-               n_groups=0, topk_groups=0, combine=COMBINE_AUTO) -> Shape:
+               n_groups=0, topk_groups=0, combine=COMBINE_AUTO, hidden_split=False) -> Shape:
     """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared").
     n_groups / topk_groups: group-limited routing (0 = off).
-    combine: COMBINE_* or its name ("auto", "grouped", "fused")."""
+    combine: COMBINE_* or its name ("auto", "grouped", "fused").
+    hidden_split: keep the SwiGLU hidden activation as two bf16 terms."""
     if isinstance(overflow, str):
         overflow = OVERFLOW[overflow]
     if isinstance(combine, str):
         combine = COMBINE[combine]
     return Shape(int(T), int(d), int(E), int(top_k), int(d_ff), int(capacity), int(act_dtype),
                  int(w_dtype), int(kind), int(bool(has_shared)), int(overflow),
-                 int(reroute_rounds), int(n_groups), int(topk_groups), int(combine))
+                 int(reroute_rounds), int(n_groups), int(topk_groups), int(combine),
+                 int(bool(hidden_split)))
 
 
 def make_weights(**tensors) -> Weights:

@@ -52,6 +52,8 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     return fail(MOE_ERR_INVALID, "reroute_rounds=%d must be in [0, 1024]", s->reroute_rounds);
   if (s->overflow == MOE_OVERFLOW_SHARED && !s->has_shared)
     return fail(MOE_ERR_INVALID, "overflow to the shared expert needs has_shared");
+  if (s->hidden_split < 0 || s->hidden_split > 1)
+    return fail(MOE_ERR_INVALID, "hidden_split=%d must be 0 or 1", s->hidden_split);
   if (s->combine < MOE_COMBINE_AUTO || s->combine > MOE_COMBINE_FUSED)
     return fail(MOE_ERR_INVALID, "combine=%d is not a moe_combine_form", s->combine);
   if (s->n_groups < 0 || s->n_groups > 64)
@@ -83,7 +85,8 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
       const int64_t A = s->T * (int64_t)s->top_k;
       const int64_t P_max = s->capacity < 0 ? A : std::min<int64_t>(A, (int64_t)s->E * s->capacity);
       const int64_t H_rows = P_max + (s->has_shared ? s->T : 0);
-      if (s->T * (int64_t)s->d * 2 > lim || H_rows * (int64_t)s->d_ff * 2 > lim ||
+      if (s->T * (int64_t)s->d * 2 > lim ||
+          H_rows * (int64_t)s->d_ff * 2 * (s->hidden_split ? 2 : 1) > lim ||
           (int64_t)s->d * s->d_ff * 2 > lim)
         return fail(MOE_ERR_UNSUPPORTED, "an operand exceeds 2 GiB (x, hidden rows or one expert matrix)");
     }
@@ -232,7 +235,8 @@ WsLayout ws_layout(const moe_shape& s) {
   L.off_slot_pos = off;
   off = align256(off + (size_t)std::max<int64_t>(A, 1) * sizeof(int32_t));
   L.off_H = off;
-  if (s.kind == MOE_EXPERT_SWIGLU) off = align256(off + (size_t)L.H_rows * s.d_ff * 2);
+  if (s.kind == MOE_EXPERT_SWIGLU)
+    off = align256(off + (size_t)L.H_rows * s.d_ff * 2 * (s.hidden_split ? 2 : 1));
   // partial tiles of split tail tiles (gate/up with a long K, the grouped-
   // output down projection with a long K)
   L.slab_floats = gemm_slab_floats(s, L.P_max);

@@ -53,6 +53,13 @@
 #include "moe_internal.h"
 #include "tile_sched.h"
 
+#ifndef MOE_SCHED_GN
+#define MOE_SCHED_GN 8
+#endif
+#ifndef MOE_SCHED_NFAST
+#define MOE_SCHED_NFAST 0
+#endif
+
 namespace moe {
 namespace {
 
@@ -86,8 +93,12 @@ struct GemmParams {
   int64_t P_max;
   int E;
   int has_shared;
-  int K;
+  int K;                      // A row length and K extent (elements)
+  int kb_len;                 // B row length (elements): K, or K/2 when A holds two
+                              // terms per hidden unit (hi | lo) against the same B
   int N;
+  int h_ld;                   // GATEUP: H row stride (N, or 2N with the lo terms after)
+  int h_split;                // GATEUP: also store lo = bf16(h - bf16(h)) at column N + n
   int mt_max;                 // upper bound of the row tiles (grid size)
   int nt;                     // weight tiles
   int split_max;              // K ranges a tail tile may be cut into (1: none)
@@ -97,6 +108,7 @@ struct GemmParams {
   int64_t slab_floats;        //   its size in floats
   int slab_piece;             //   floats per partial tile: activation-tile rows x 256
   int group_n;                // weight tiles per expert-aligned block of the tile order
+  int nfast;                  // tile order inside a block: weight tiles fastest (1) or row tiles
   int krot;                   // K walk start of workgroup b: (b * krot) mod (its K steps); 0 = none
   float* zero_out;            // zero_n floats (16-byte aligned) the workgroups clear first, or NULL
   int64_t zero_n;             //   (the atomic combine's y, cleared by the gate/up launch)
@@ -193,7 +205,7 @@ __device__ __forceinline__ void tile_place(const GemmParams& p, const int* s_pre
                                            TileMap& t) {
   const int nseg = p.E + (p.has_shared ? 1 : 0);
   int seg = 0, mslot = 0, ntile = 0;
-  sched_tile_of(q, s_pre, nseg, p.nt, p.group_n, seg, mslot, ntile);
+  sched_tile_of(q, s_pre, nseg, p.nt, p.group_n, seg, mslot, ntile, p.nfast != 0);
   t.e = __builtin_amdgcn_readfirstlane(seg);
   t.ntile = __builtin_amdgcn_readfirstlane(ntile);
   t.m0 = __builtin_amdgcn_readfirstlane((mslot - s_pre[seg]) * BM);
@@ -234,6 +246,23 @@ __device__ __forceinline__ int64_t a_row(const GemmParams& p, const TileMap& t, 
   return t.shared_e ? p.P_max + m : (int64_t)t.seg + m;
 }
 
+// Four consecutive hidden values h[0..3] of one row at column n: their bf16
+// roundings hi, and with `split` also lo = bf16(h - hi) at column N + n (the
+// compensated form, h = hi + lo to about 2^-17 relative).
+__device__ __forceinline__ void store_h4(uint16_t* hrow, int n, int N, const float (&h)[4],
+                                         int split) {
+  uint32_t hb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16_bits(h[r]);
+  *(uint2*)(hrow + n) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+  if (split) {
+    uint32_t lb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lb[r] = f32_to_bf16_bits(h[r] - bf16_bits_to_f32(hb[r]));
+    *(uint2*)(hrow + N + n) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+  }
+}
+
 // Epilogue.  32x32 accumulator register r of lane l is row (r/4)*8 +
 // (l/32)*4 + r%4, column l%32 of the 32x32 tile.  arow0: the wave's first
 // activation row in the tile, its i-th 32-row granule starting RS rows
@@ -262,7 +291,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
       const int m = t.m0 + arow0 + i * RS + ccol;
       if (m >= t.rows || m - t.m0 >= TR) continue;
       const float cr = CORR ? ctab[i * 32 + ccol] : 0.f;
-      uint16_t* hrow = p.H + (hbase + m) * N;
+      uint16_t* hrow = p.H + (hbase + m) * p.h_ld;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -285,17 +314,14 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, f32x16 (&acc)[4]
                 (acc[i][j + 2][q * 4 + 2] - cr) * su, (acc[i][j + 2][q * 4 + 3] - cr) * su);
             continue;
           }
-          uint32_t hb[4];
+          float hv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float a = (acc[i][j][q * 4 + r] - cr) * sg;
             const float g = (acc[i][j + 2][q * 4 + r] - cr) * su;
-            hb[r] = f32_to_bf16_bits(a / (1.f + __expf(-a)) * g);
+            hv[r] = a / (1.f + __expf(-a)) * g;
           }
-          uint2 v;
-          v.x = hb[0] | (hb[1] << 16);
-          v.y = hb[2] | (hb[3] << 16);
-          *(uint2*)(hrow + n) = v;
+          store_h4(hrow, n, N, hv, p.h_split);
         }
       }
     }
@@ -506,10 +532,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = p.K, N = p.N;
+  const int K = p.K, N = p.N, KW = p.kb_len;
   // K steps of KB (the workgroup's K range is given in steps of BK)
   const int kbeg_el = t.kbeg * BK;
   const int nk = (t.nk * BK) / KB;
+  // B's K steps: step kabs of A reads B step kabs mod nkw (A holding two
+  // terms per hidden unit reads B twice)
+  const int nkw = KW / KB;
+  const int kbeg_st = kbeg_el / KB;
 
   // ---- DMA sources.  Waves 0, 1 fill the A tile, waves 2, 3 the B tile
   // (in GATEUP wave 2 the W1 rows, wave 3 the W3 rows).  A wave's
@@ -517,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // lane / CPR (B: the _B / CPRB / NIB counterparts); lane i writes chunk slot
   // i % CPR, which holds K chunk (i % CPR) ^ swz(row).
   const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
-  const int64_t ebytes = (int64_t)N * K * WBITS / 8;
+  const int64_t ebytes = (int64_t)N * KW * WBITS / 8;
   const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
   // the B wave's own weight matrix (GATEUP: wave 3 reads W3, wave 2 W1), as
   // one resource built from a pointer chosen up front (a select between two
@@ -546,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       const int r = ((wave & 1) * C::NIB + j) * C::ROWS_PER_INST_B + lane / C::CPRB;
       const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
       const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + min(r, 255);
-      voff[j] = n < N ? (uint32_t)(((int64_t)n * K + kbeg_el) * WBITS / 8 + chunk * 16) : kOobOff;
+      voff[j] = n < N ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
     }
   });
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
@@ -573,7 +603,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     char* gbase = dlds + stage * C::STAGE_BYTES +
                   (a_wave ? (wave & 1) * (C::TILE_BYTES / 2)
                           : C::TILE_BYTES + (wave & 1) * (C::B_TILE_BYTES / 2));
-    const int soff = __builtin_amdgcn_readfirstlane(kr * (a_wave ? C::RB : C::RBB));
+    int kb = kbeg_st + kr;  // B: the absolute step, wrapped
+    kb = kb >= nkw ? kb - nkw : kb;
+    const int soff = __builtin_amdgcn_readfirstlane(a_wave ? kr * C::RB : kb * C::RBB);
     if constexpr (C::NI == C::NIB) {
       static_for<C::NI>([&](auto j) {
         if (j < a_valid)
@@ -881,13 +913,10 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmParams p) {
     if (MODE == MODE_GATEUP) {
       const float g[4] = {a[v].x, a[v].y, a[v].z, a[v].w};
       const float up[4] = {u[v].x, u[v].y, u[v].z, u[v].w};
-      uint32_t hb[4];
+      float hv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16_bits(g[q] / (1.f + __expf(-g[q])) * up[q]);
-      uint2 w;
-      w.x = hb[0] | (hb[1] << 16);
-      w.y = hb[2] | (hb[3] << 16);
-      *(uint2*)(p.H + (obase + row[v]) * p.N + n0 + col[v]) = w;
+      for (int q = 0; q < 4; ++q) hv[q] = g[q] / (1.f + __expf(-g[q])) * up[q];
+      store_h4(p.H + (obase + row[v]) * p.h_ld, n0 + col[v], p.N, hv, p.h_split);
     } else {
       *(float4*)(p.y_perm + (obase + row[v]) * p.N + n0 + col[v]) = a[v];
     }
@@ -1115,7 +1144,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.mt_max = (int)mt_bound;
   g.tail_slab = tail_slab;
   g.slab_floats = L.slab_floats;
-  g.group_n = 8;  // weight tiles per expert-aligned block of the tile order
+  g.group_n = MOE_SCHED_GN;  // weight tiles per expert-aligned block of the tile order
+  g.nfast = MOE_SCHED_NFAST;
 
   // gate / up (it also clears y for the atomic combine when asked)
   if (zero_y && y) {
@@ -1128,7 +1158,10 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g.sc0 = w.s1; g.sc1 = w.s3; g.sc0s = w.s1s; g.sc1s = w.s3s;
   g.H = (uint16_t*)H;
   g.K = s.d;
+  g.kb_len = s.d;
   g.N = s.d_ff;
+  g.h_split = s.hidden_split ? 1 : 0;
+  g.h_ld = s.d_ff * (g.h_split ? 2 : 1);
   const int bn1 = 128;  // hidden columns per gate/up tile (128 of W1 + 128 of W3)
   g.nt = (s.d_ff + bn1 - 1) / bn1;
   // tail tiles split over K through the slab + fixup (SwiGLU needs whole
@@ -1154,15 +1187,17 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   g2.zero_out = nullptr;
   g2.zero_n = 0;
   g2.A = (const uint16_t*)H;
-  g2.A_bytes = L.H_rows * (int64_t)s.d_ff * 2;
+  g2.A_bytes = L.H_rows * (int64_t)g.h_ld * 2;
   g2.B0 = w.W2; g2.B1 = nullptr; g2.B0s = w.W2s; g2.B1s = nullptr;
   g2.sc0 = w.s2; g2.sc1 = nullptr; g2.sc0s = w.s2s; g2.sc1s = nullptr;
   g2.H = nullptr;
   g2.y = y;
   g2.y_perm = y_perm;
   g2.shared_w = shared_w;
-  g2.K = s.d_ff;
+  g2.K = g.h_ld;  // hi | lo: K = 2 d_ff over the same W2 rows
+  g2.kb_len = s.d_ff;
   g2.N = s.d;
+  g2.h_split = 0;
   const int bn2 = 256;  // output columns per down tile
   g2.nt = (s.d + bn2 - 1) / bn2;
   g2.mt_max = (int)mt_bound;

@@ -8,10 +8,11 @@
 //  * Real tiles are numbered densely, q = 0 .. R-1 with R = Mreal * nt
 //    (Mreal row tiles summed over the expert segments, nt weight tiles), in
 //    expert-aligned blocks: the weight tiles are taken in groups of gn, and
-//    inside a group segment by segment, all row tiles of the segment
-//    (fastest) times the group's weight tiles.  Consecutive q then share the
-//    segment's weight panels and its activation rows; a block never mixes two
-//    experts' weights.
+//    inside a group segment by segment, all row tiles of the segment times
+//    the group's weight tiles, either row tiles fastest (consecutive q share
+//    a weight panel) or weight tiles fastest (nfast: the gn consecutive q of
+//    one row tile share its activation rows, and do the same work, so they
+//    run in step).  A block never mixes two experts' weights.
 //  * Workgroup ids are dealt round-robin to the XCDs; XCD x takes the
 //    contiguous q range [R x / X, R (x+1) / X), so every XCD gets the same
 //    number of tiles (+-1) and its concurrent workgroups stay inside one or
@@ -46,7 +47,7 @@ struct SchedUnit {
 // prefix sum of the segments' row tiles, pre[nseg] = Mreal); empty segments
 // are allowed.
 constexpr void sched_tile_of(int64_t q, const int* pre, int nseg, int nt, int gn, int& seg,
-                             int& mslot, int& ntile) {
+                             int& mslot, int& ntile, bool nfast = false) {
   const int Mreal = pre[nseg];
   const int64_t col = (int64_t)Mreal * gn;  // tiles per full weight-tile group
   const int ng = (int)(q / col);
@@ -61,8 +62,13 @@ constexpr void sched_tile_of(int64_t q, const int* pre, int nseg, int nt, int gn
   seg = lo;
   const int me = pre[seg + 1] - pre[seg];
   const int64_t loc = r - (int64_t)pre[seg] * nh;
-  mslot = pre[seg] + (int)(loc % me);
-  ntile = ng * gn + (int)(loc / me);
+  if (nfast) {
+    mslot = pre[seg] + (int)(loc / nh);
+    ntile = ng * gn + (int)(loc % nh);
+  } else {
+    mslot = pre[seg] + (int)(loc % me);
+    ntile = ng * gn + (int)(loc / me);
+  }
 }
 
 // The K-range split of the tail round: pieces per tile for `rem` tiles on

@@ -21,17 +21,20 @@ class MoELayer:
     fate of assignments past the capacity.  n_groups / topk_groups: group-
     limited routing (each token uses at most topk_groups groups).  combine:
     "auto", "grouped" or "fused", the form of the combine (moe_combine_form).
+    hidden_split: the compensated hidden activation (moe_shape.hidden_split).
     """
 
     def __init__(self, T, d, E, top_k, d_ff, *, W_g, b_g=None, weights, capacity=-1,
                  kind="swiglu", w_dtype="bf16", has_shared=False, overflow="drop",
-                 reroute_rounds=0, n_groups=0, topk_groups=0, combine="auto", device="cuda"):
+                 reroute_rounds=0, n_groups=0, topk_groups=0, combine="auto", hidden_split=False,
+                 device="cuda"):
         self.kind = SWIGLU if kind == "swiglu" else LINEAR_BIAS
         act = DT_BF16 if self.kind == SWIGLU else DT_F32
         wdt = {"bf16": DT_BF16, "fp8_e4m3": DT_FP8_E4M3, "int8": DT_INT8, "int4": DT_INT4,
                "f32": DT_F32}[w_dtype]
         self.shape = make_shape(T, d, E, top_k, d_ff, capacity, act, wdt, self.kind, has_shared,
-                                overflow, reroute_rounds, n_groups, topk_groups, combine)
+                                overflow, reroute_rounds, n_groups, topk_groups, combine,
+                                hidden_split)
         self.W_g = W_g
         self.b_g = b_g
         self.weights = make_weights(**weights)

@@ -33,6 +33,7 @@ class MoEConfig:
     seed: int = SEED_BASE
     x_from: Optional[str] = None     # take x as the first T rows of this config's x
     w_from: Optional[str] = None     # take all weights from this config
+    hidden_split: bool = False       # the layer keeps its hidden activation as two bf16 terms
 
     @property
     def A(self) -> int:
@@ -75,7 +76,7 @@ CONFIGS = {
     "capacity_skew": MoEConfig("capacity_skew", T=16384, d=4096, E=64, k=2,
                                d_ff=1408, kind="swiglu", act="bf16", w="bf16",
                                cf=1.25, router_bias="zipf1.5",
-                               seed=SEED_BASE + 5),
+                               seed=SEED_BASE + 5, hidden_split=True),
 }
 
 
@@ -85,7 +86,7 @@ def get_config(name: str) -> MoEConfig:
 
 def custom_config(T, d, E, k, d_ff=0, *, kind="swiglu", act="bf16", w="bf16",
                   cf=None, router_bias=None, shared=False, seed=12345,
-                  name="custom") -> MoEConfig:
+                  name="custom", hidden_split=False) -> MoEConfig:
     return MoEConfig(name, T=T, d=d, E=E, k=k, d_ff=d_ff, kind=kind, act=act,
                      w=w, cf=cf, router_bias=router_bias, shared=shared,
-                     seed=seed)
+                     seed=seed, hidden_split=hidden_split)

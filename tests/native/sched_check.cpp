@@ -16,7 +16,7 @@
 using namespace moe;
 
 static int check(const std::vector<int>& tiles_per_seg, int nt, int gn, int kunits, int slots,
-                 int split_max) {
+                 int split_max, bool nfast) {
   const int nseg = (int)tiles_per_seg.size();
   std::vector<int> pre(nseg + 1, 0);
   for (int s = 0; s < nseg; ++s) pre[s + 1] = pre[s] + tiles_per_seg[s];
@@ -36,7 +36,7 @@ static int check(const std::vector<int>& tiles_per_seg, int nt, int gn, int kuni
       }
       ++units;
       int seg = -1, m = -1, n = -1;
-      sched_tile_of(u.q, pre.data(), nseg, nt, gn, seg, m, n);
+      sched_tile_of(u.q, pre.data(), nseg, nt, gn, seg, m, n, nfast);
       if (u.q < 0 || u.q >= R || seg < 0 || seg >= nseg || m < pre[seg] || m >= pre[seg + 1] ||
           n < 0 || n >= nt || u.nk <= 0 || u.kbeg < 0 || u.kbeg + u.nk > kunits) {
         printf("FAIL bad unit M=%d nt=%d gn=%d x=%d i=%lld -> q=%lld seg=%d m=%d n=%d k=%d+%d\n",
@@ -74,7 +74,7 @@ static int check(const std::vector<int>& tiles_per_seg, int nt, int gn, int kuni
   // the tile map alone is a bijection q <-> (row tile, weight tile)
   for (int64_t q = 0; q < R; ++q) {
     int seg = -1, m = -1, n = -1;
-    sched_tile_of(q, pre.data(), nseg, nt, gn, seg, m, n);
+    sched_tile_of(q, pre.data(), nseg, nt, gn, seg, m, n, nfast);
     tile_seen[(size_t)m * nt + n]++;
   }
   for (size_t c = 0; c < tile_seen.size(); ++c)
@@ -110,8 +110,10 @@ int main() {
             for (int sl : slotss)
               for (int sp : splits) {
                 if (nseg * nt > 4000 && (ku > 7 || sl != 32)) continue;  // keep it quick
-                if (check(tps, nt, gn, ku, sl, sp < ku ? sp : ku)) return 1;
-                ++cases;
+                for (int nf = 0; nf < 2; ++nf) {
+                  if (check(tps, nt, gn, ku, sl, sp < ku ? sp : ku, nf != 0)) return 1;
+                  ++cases;
+                }
               }
     }
   // expert-aligned blocks: with segments of 4 row tiles and gn = 8, the first
@@ -122,6 +124,16 @@ int main() {
     sched_tile_of(q, pre.data(), 3, 112, 8, seg, m, n);
     if (seg != 0 || m != (int)(q % 4) || n != (int)(q / 4)) {
       printf("FAIL block order q=%lld -> seg %d m %d n %d\n", (long long)q, seg, m, n);
+      return 1;
+    }
+  }
+  // weight tiles fastest: the first 32 tiles are row tiles 0..3 of segment 0,
+  // each with weight tiles 0..7
+  for (int64_t q = 0; q < 32; ++q) {
+    int seg = -1, m = -1, n = -1;
+    sched_tile_of(q, pre.data(), 3, 112, 8, seg, m, n, true);
+    if (seg != 0 || m != (int)(q / 8) || n != (int)(q % 8)) {
+      printf("FAIL nfast block order q=%lld -> seg %d m %d n %d\n", (long long)q, seg, m, n);
       return 1;
     }
   }

@@ -90,7 +90,8 @@ def gpu_forward(wl: Workload, dev=None, overflow="drop", rounds=0, groups=0, top
     layer = moe.MoELayer(c.T, c.d, c.E, c.k, c.d_ff, W_g=dev["W_g"], b_g=dev["b_g"],
                          weights=dev["weights"], capacity=cap, kind=c.kind, w_dtype=c.w,
                          has_shared=c.shared, overflow=overflow, reroute_rounds=rounds,
-                         n_groups=groups, topk_groups=topk_groups, combine=combine)
+                         n_groups=groups, topk_groups=topk_groups, combine=combine,
+                         hidden_split=c.hidden_split)
     layer(dev["x"])
     torch.cuda.synchronize()
     out = dict(y=layer.y.cpu().numpy(), idx=layer.topk_idx.cpu().numpy(),

@@ -97,6 +97,35 @@ def test_forward_small(moe, T, d, E, k, d_ff, cf, shared, w, bias):
     print(f"  err={rep['err']:.3e} flipped={rep['flipped']} kept={rep['kept']}", flush=True)
 
 
+@pytest.mark.parametrize("T,d,E,k,d_ff,cf,shared,w,bias", [
+    (777, 512, 8, 2, 256, 1.0, False, "bf16", "zipf1.5"),
+    (600, 512, 4, 2, 4096, None, True, "bf16", None),        # split tail tiles, fixup
+    (300, 4096, 4, 2, 256, None, True, "bf16", None),        # gate/up fixup writes lo too
+    (64, 512, 8, 2, 1408, None, False, "bf16", None),        # decode-sized, fused combine
+    (500, 256, 8, 2, 256, None, True, "fp8_e4m3", None),
+    (1100, 512, 8, 2, 384, None, True, "int4", None),
+    (96, 256, 16, 2, 384, 0.75, True, "int8", "zipf1.5")])
+def test_forward_hidden_split(moe, T, d, E, k, d_ff, cf, shared, w, bias):
+    """The compensated hidden activation (hi + lo bf16 terms): the same
+    routing, and y much closer to the oracle than with a bf16 hidden
+    activation (whose rounding then dominates the error), in every weight
+    format and pipeline shape."""
+    print(f"[hidden split] T={T} d={d} E={E} k={k} d_ff={d_ff} cf={cf} shared={shared} w={w}",
+          flush=True)
+    base = custom_config(T, d, E, k, d_ff, w=w, cf=cf, shared=shared, router_bias=bias,
+                         seed=T + d + E + 1)
+    wl1 = Workload(base)
+    out1, _, dev = gpu_forward(wl1)
+    rep1 = check_forward(wl1, out1)
+    wl2 = Workload(base.with_(hidden_split=True))
+    out2, _, _ = gpu_forward(wl2, dev=dev)
+    rep2 = check_forward(wl2, out2)
+    assert np.array_equal(out1["idx"], out2["idx"]) and np.array_equal(out1["counts"], out2["counts"])
+    print(f"  err bf16 h {rep1['err']:.3e}, compensated h {rep2['err']:.3e}", flush=True)
+    if w == "bf16":
+        assert rep2["err"] < rep1["err"] / 20
+
+
 def test_tiny_page_layer(moe):
     """The tutorial-sized fp32 layer: 64 tokens, width 8, 4 Linear experts, top-2."""
     wl = Workload(get_config("tiny"))

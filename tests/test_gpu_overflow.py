@@ -126,7 +126,7 @@ FORWARD = [
     (1000, 256, 8, 2, 256, 1.0, False, "bf16", "zipf1.5", "reroute", 1, None),
     (1000, 256, 8, 2, 256, 1.0, False, "bf16", "zipf1.5", "reroute", 6, None),
     (777, 512, 16, 4, 128, 0.75, True, "bf16", "zipf1.5", "reroute", 2, "grouped"),
-    (777, 512, 16, 4, 128, 0.75, True, "bf16", "zipf1.5", "reroute", 2, "atomic"),
+    (777, 512, 16, 4, 128, 0.75, True, "bf16", "zipf1.5", "reroute", 2, "fused"),
     (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5", "reroute", 3, None),
     (600, 256, 8, 2, 256, 1.0, True, "bf16", "zipf1.5", "shared", 0, "grouped"),
     (600, 256, 8, 2, 256, 1.0, True, "bf16", "zipf1.5", "shared", 0, "fused"),

@@ -291,6 +291,28 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g,
                        int32_t* topk_idx, float* topk_w, int32_t* counts,
                        int32_t* offsets, void* ws, void* stream);
 
+/* Size of the fixed device scratch moe_forward_noalloc uses: 64 MiB, one copy
+ * per device the library runs on, held until the process ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as moe_forward,
+ * minus `ws`: the library's fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES
+ * on the current device stands in for it.  Shapes whose
+ * moe_workspace_bytes() exceed that size are rejected with
+ * MOE_ERR_UNSUPPORTED before anything is launched (decode-sized batches fit:
+ * T = 64 at d = 4096, E = 8, d_ff = 14336 needs about 20 MiB).  This entry
+ * point calls no allocating routine; the first call on a device looks up the
+ * scratch array's device address once.  Every call on a device shares that
+ * device's scratch: calls that overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs to start at zero; stage timing is not recorded. */
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* W_g,
+                               const float* b_g, const moe_weights* w, float* y,
+                               int32_t* topk_idx, float* topk_w, int32_t* counts,
+                               int32_t* offsets, void* stream);
+
 /* Load imbalance [host] (tutorial §4.2 expert_imbalance):
  * max(load) / (min(load) + 1e-6).  Returns -1 for E <= 0 or load == NULL. */
 double moe_load_imbalance(const int64_t* load, int32_t E);

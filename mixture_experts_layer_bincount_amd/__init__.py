@@ -32,6 +32,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_E
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_from_logits",
            "moe_reroute", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_forward_noalloc",
            "moe_load_imbalance", "moe_lpt_pack", "moe_eplb_plan", "moe_timing_enable",
            "moe_timing_collect",
            "moe_timing_stage_name", "moe_last_error")
@@ -80,6 +81,8 @@ _lib.moe_combine.restype = ctypes.c_int
 _lib.moe_combine.argtypes = [_P(Shape)] + [_vp] * 5
 _lib.moe_forward.restype = ctypes.c_int
 _lib.moe_forward.argtypes = [_P(Shape), _vp, _vp, _vp, _P(Weights)] + [_vp] * 7
+_lib.moe_forward_noalloc.restype = ctypes.c_int
+_lib.moe_forward_noalloc.argtypes = [_P(Shape), _vp, _vp, _vp, _P(Weights)] + [_vp] * 6
 _lib.moe_load_imbalance.restype = ctypes.c_double
 _lib.moe_load_imbalance.argtypes = [_P(ctypes.c_int64), ctypes.c_int32]
 _lib.moe_lpt_pack.restype = ctypes.c_int
@@ -243,6 +246,17 @@ def moe_forward(shape, x, W_g, b_g, weights, y, topk_idx, topk_w, counts, offset
     _check(_lib.moe_forward(ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g),
                             ctypes.byref(weights), _ptr(y), _ptr(topk_idx), _ptr(topk_w),
                             _ptr(counts), _ptr(offsets), _ptr(ws), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(shape, x, W_g, b_g, weights, y, topk_idx, topk_w, counts, offsets,
+                        stream=None):
+    _check(_lib.moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g),
+                                    ctypes.byref(weights), _ptr(y), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                                    _stream(stream)))
 
 
 from .layer import MoELayer  # noqa: E402,F401

@@ -432,9 +432,16 @@ moe_status moe_combine(const moe_shape* shape, const float* y_perm, const int32_
                     "combine");
 }
 
-moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, const float* b_g,
-                       const moe_weights* w, float* y, int32_t* topk_idx, float* topk_w,
-                       int32_t* counts, int32_t* offsets, void* ws, void* stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// The layer's launch sequence over a workspace `ws` of ws_layout(*shape)
+// bytes.  `timed`: record the stage events when stage timing is enabled.
+moe_status forward_impl(const moe_shape* shape, const void* x, const float* W_g, const float* b_g,
+                        const moe_weights* w, float* y, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, void* ws, void* stream, bool timed) {
   MOE_TRY(check_shape(shape, true));
   const moe_shape& s = *shape;
   if (s.E > 256 && !router_mfma_epad(s))
@@ -458,7 +465,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   MOE_TRY(check_ptr(topk_w, "topk_w"));
   MOE_TRY(check_weights(&s, w));
   CallEvents ce;
-  ce.begin(st);
+  if (timed) ce.begin(st);
   MOE_TRY(hip_status(launch_router_gemm(s, x, W_g, W.partial, L.router_splits, W.wsplit, st), "router gemm"));
   ce.mark(1, st);
   // re-routing: the top-k kernel also lists each token's further candidates
@@ -516,6 +523,63 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, 
   ce.mark(6, st);
   ce.finish();
   return r;
+}
+
+// ---- the allocation-free variant of moe_forward: a fixed scratch array in
+// device memory (one copy per device, held until the process ends) in place
+// of the caller's workspace.  Host code never passes the array's name to a
+// kernel: it uses the device address hipGetSymbolAddress gives, per device.
+constexpr size_t kNoallocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+struct ScratchAddress {
+  std::once_flag once[kMaxDevices];
+  hipError_t err[kMaxDevices] = {};
+  void* ptr[kMaxDevices] = {};
+};
+ScratchAddress g_scratch;
+
+// The current device's copy of `scratch`, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch.once[dev], [&] {
+    g_scratch.err[dev] = hipGetSymbolAddress(&g_scratch.ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch.err[dev] != hipSuccess) return g_scratch.err[dev];
+  *out = g_scratch.ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* W_g, const float* b_g,
+                       const moe_weights* w, float* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* offsets, void* ws, void* stream) {
+  return forward_impl(shape, x, W_g, b_g, w, y, topk_idx, topk_w, counts, offsets, ws, stream,
+                      /*timed=*/true);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* W_g,
+                               const float* b_g, const moe_weights* w, float* y,
+                               int32_t* topk_idx, float* topk_w, int32_t* counts,
+                               int32_t* offsets, void* stream) {
+  MOE_TRY(check_shape(shape, true));
+  const size_t need = ws_layout(*shape).total;
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: this shape needs %zu bytes of scratch, more than the "
+                "library's fixed %zu (use moe_forward with a workspace)",
+                need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  MOE_TRY(hip_status(scratch_address(&ws), "scratch address"));
+  return forward_impl(shape, x, W_g, b_g, w, y, topk_idx, topk_w, counts, offsets, ws, stream,
+                      /*timed=*/false);
 }
 
 double moe_load_imbalance(const int64_t* load, int32_t E) {

@@ -59,6 +59,12 @@
 #ifndef MOE_SCHED_NFAST
 #define MOE_SCHED_NFAST 0
 #endif
+#ifndef MOE_GEMM_PF
+#define MOE_GEMM_PF 0
+#endif
+#ifndef MOE_GEMM_PP
+#define MOE_GEMM_PP 1
+#endif
 
 namespace moe {
 namespace {
@@ -168,11 +174,11 @@ constexpr int kMaxSegments = 1025;  // routed experts (at most 1024) + shared
 // Row tiles per segment (routed experts, then the shared expert), counted
 // from the device-side offsets and scanned into s_pre (s_pre[nseg] = total).
 // Must be called by all threads of the workgroup; returns the total.
-template <int BM>
+template <int BM, int NT = 256>
 __device__ __forceinline__ int seg_prefix(const GemmParams& p, int* s_pre, int* s_scan) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nseg = p.E + (p.has_shared ? 1 : 0);
-  const int per = (nseg + 255) / 256;
+  const int per = (nseg + NT - 1) / NT;
   const int e_lo = tid * per;
   auto seg_tiles = [&](int e) {
     const int64_t rows = (e < p.E) ? (int64_t)(p.offsets[e + 1] - p.offsets[e]) : p.T;
@@ -194,7 +200,11 @@ __device__ __forceinline__ int seg_prefix(const GemmParams& p, int* s_pre, int* 
       run += seg_tiles(e);
     }
   }
-  if (tid == 0) s_pre[nseg] = s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
+  if (tid == 0) {
+    int total = 0;
+    for (int w2 = 0; w2 < NT / 64; ++w2) total += s_scan[w2];
+    s_pre[nseg] = total;
+  }
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(s_pre[nseg]);
 }
@@ -218,11 +228,11 @@ __device__ __forceinline__ void tile_place(const GemmParams& p, const int* s_pre
 // The workgroup's unit of the tile schedule (tile_sched.h) over the
 // expert-aligned tile order.  Returns false when the workgroup has no unit.
 // Must be called by all threads of the workgroup.
-template <int MODE, int BM>
+template <int MODE, int BM, int NT = 256>
 __device__ __forceinline__ bool map_tile(const GemmParams& p, TileMap& t) {
-  __shared__ int s_scan[4];
+  __shared__ int s_scan[NT / 64];
   __shared__ int s_pre[kMaxSegments + 1];
-  const int Mreal = seg_prefix<BM>(p, s_pre, s_scan);
+  const int Mreal = seg_prefix<BM, NT>(p, s_pre, s_scan);
   SchedUnit u{};
   const int kunits = p.K / BK / p.kunit;
   const int xcd = (int)(blockIdx.x % kNumXcd);
@@ -514,8 +524,17 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <int MODE, int KB, int NS, int MOE_AUX, int WQ, int BMA>
+// L2 prefetch (PF = 1): when a workgroup issues the DMA of K step s, it also
+// touches every 128-byte line of step s + 1 of its A and B rows with one
+// 4-byte DMA per row into a sink in LDS that nothing reads, so those lines
+// are on their way to L2 a step before their DMA and that DMA hits L2.  A
+// 64-deep step of a row is exactly one line, so 512 rows take 8 instructions
+// (2 per wave) and 2 KiB of sink.
+constexpr int kPfSinkBytes = 2048;
+
+template <int MODE, int KB, int NS, int MOE_AUX, int WQ, int BMA, int PF = 0>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  static_assert(!PF || (KB * 2 == 128 && BMA == 256 && NS == 2), "prefetch: 64-deep bf16 steps, 256-row tiles");
   constexpr bool FP8 = WQ != WQ_BF16;  // quantised weight codes with scales
   constexpr int WBITS = wq_bits(WQ);
   using C = DmaCfg<KB, NS, WBITS, BMA>;
@@ -579,6 +598,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       voff[j] = n < N ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
     }
   });
+  // prefetch rows: A waves their 128 activation rows, B waves their 128 weight
+  // rows, lane + 64 j for j = 0, 1
+  uint32_t pfoff[2] = {kOobOff, kOobOff};
+  if constexpr (PF != 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = (wave & 1) * 128 + j * 64 + lane;
+      if (a_wave) {
+        const int m = t.m0 + r;
+        pfoff[j] = m < t.rows ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2) : kOobOff;
+      } else {
+        const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+        pfoff[j] = n < N ? (uint32_t)((int64_t)n * KW * WBITS / 8) : kOobOff;
+      }
+    }
+  }
   // Branching on the (scalar) wave index keeps each resource in scalar registers.
   // Activation DMA instructions whose rows all lie past the segment's end
   // are not issued at all.  A wave's rows are contiguous, so its valid
@@ -620,6 +655,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       static_for<C::NIB>([&](auto j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
+    }
+    if constexpr (PF != 0) {
+      // the next step's lines (issued after this step's DMA, so waiting for
+      // this step leaves these two in flight)
+      if (kt + 1 < nk) {
+        const int kq = kt + 1 + krot < nk ? kt + 1 + krot : kt + 1 + krot - nk;
+        int kbq = kbeg_st + kq;
+        kbq = kbq >= nkw ? kbq - nkw : kbq;
+        const int spf = __builtin_amdgcn_readfirstlane(a_wave ? kq * C::RB : kbq * C::RBB);
+        char* sink = dlds + C::LDS + wave * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)sink, 4, pfoff[0], spf, 0, MOE_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(sink + 256), 4, pfoff[1], spf, 0, MOE_AUX);
+      }
     }
   };
 
@@ -682,8 +730,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     const int t = sl / HPS;
     wait_lgkm0();
     // steady state: the NS - 2 later steps may stay in flight; near the end
-    // (fewer issued) wait for everything
-    if (t + NS - 2 <= nk - 1)
+    // (fewer issued) wait for everything.  With the prefetch the two touches
+    // of step t + 1, issued after step t's DMA, may stay in flight.
+    if (PF != 0 && t + 1 < nk)
+      wait_vmcnt<2>();
+    else if (t + NS - 2 <= nk - 1)
       wait_steps(std::integral_constant<int, NS - 2>{});
     else
       wait_vmcnt<0>();
@@ -773,7 +824,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     static_for<NS - 1>([&](auto s) {
       if (s < nk) issue(s, s);
     });
-    if (NS - 2 >= 2 && nk > 2)
+    if (PF != 0 && nk > 1)
+      wait_vmcnt<2>();
+    else if (NS - 2 >= 2 && nk > 2)
       wait_steps(std::integral_constant<int, 2>{});
     else if (NS - 2 >= 1 && nk > 1)
       wait_steps(std::integral_constant<int, 1>{});
@@ -819,6 +872,266 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   } else {
     store_tile<MODE, FP8, 64, DMA_BM, false, (BMA + 63) / 64, BMA>(p, acc, t, arow0, n0, wn, brow);
   }
+}
+
+
+// Epilogue of the ping-pong kernel: the wave's NG granules (activation rows
+// arow0 + 64 i + 0..31) x its two 32-row weight tiles.  MODE_GATEUP
+// (transposed product): acc[i][0] / acc[i][1] hold gate / up rows wn*32 + R of
+// the weight tile, R = (r / 4) * 8 + (lane / 32) * 4 + r % 4, for activation
+// row arow0 + 64 i + lane % 32; DOWN*: acc[i][j] holds activation row
+// arow0 + 64 i + R, output column wn*64 + 32 j + lane % 32.
+template <int MODE, int NG>
+__device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)[NG][2],
+                                              const TileMap& t, int arow0, int n0, int wn) {
+  const int lane = threadIdx.x & 63;
+  const int ccol = lane & 31;
+  const int rbase = (lane >> 5) * 4;
+  const int N = p.N;
+  if (MODE == MODE_GATEUP) {
+    const int64_t hbase = t.shared_e ? p.P_max : (int64_t)t.seg;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = t.m0 + arow0 + i * 64 + ccol;
+      if (m >= t.rows) continue;
+      uint16_t* hrow = p.H + (hbase + m) * p.h_ld;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 32 + q * 8 + rbase;  // 4 consecutive hidden columns
+        if (n >= N) continue;
+        if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
+          float* sl = p.tail_slab + (int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0);
+          *(float4*)sl = make_float4(acc[i][0][q * 4], acc[i][0][q * 4 + 1], acc[i][0][q * 4 + 2],
+                                     acc[i][0][q * 4 + 3]);
+          *(float4*)(sl + 128) = make_float4(acc[i][1][q * 4], acc[i][1][q * 4 + 1],
+                                             acc[i][1][q * 4 + 2], acc[i][1][q * 4 + 3]);
+          continue;
+        }
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = acc[i][0][q * 4 + r];
+          hv[r] = a / (1.f + __expf(-a)) * acc[i][1][q * 4 + r];
+        }
+        store_h4(hrow, n, N, hv, p.h_split);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = t.m0 + arow0 + i * 64 + q * 8 + rbase + r;
+          if (m >= t.rows) continue;
+          float wgt = 1.f;
+          int64_t orow;
+          if (MODE == MODE_DOWN) {
+            if (t.shared_e) {
+              orow = m;
+              if (p.shared_w) wgt = p.shared_w[m];
+            } else {
+              orow = p.perm_token[t.seg + m];
+              wgt = p.perm_w[t.seg + m];
+            }
+          } else {
+            orow = t.shared_e ? p.P_max + m : (int64_t)t.seg + m;
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + j * 32 + ccol;
+            if (n >= N) continue;
+            const float v = acc[i][j][q * 4 + r];
+            if (MODE == MODE_DOWN)
+              atomicAdd(&p.y[orow * N + n], wgt * v);
+            else if (t.slab >= 0)
+              p.tail_slab[(int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0)] = v;
+            else
+              p.y_perm[orow * N + n] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong kernel for bf16 weights: 256 x 256 tiles, 512 threads = 8 waves,
+// two per SIMD (wave w runs on SIMD w % 4).  Wave w computes 128 activation
+// rows (the 32-row granules (w & 1) + 2i) x 64 weight rows (quarter w >> 1;
+// in MODE_GATEUP 32 rows of W1 and the same 32 rows of W3).  Each wave
+// alternates a read phase (the 12 fragments of one 32-deep K slice, LDS ->
+// registers) and a compute phase (16 MFMAs 32x32x16 on them); waves 4..7 run
+// one phase behind waves 0..3, so on every SIMD one wave's MFMAs issue back to
+// back while the other's LDS reads are in flight.  A barrier separates the
+// phases.  Operands move global -> LDS by buffer_load ... lds in two 64-deep
+// stages (the XOR-swizzled row layout of DmaCfg): waves 0..3 fetch step u's
+// weight tile during their read of slice 2u - 2, waves 4..7 its activation
+// tile one phase later, and both wait for their own loads at the end of the
+// phase before slice 2u is first read.  Tile map, K split and the partial
+// tile slab are those of grouped_gemm_dma_kernel.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
+  using C = DmaCfg<64, 2, 16, 256>;
+  constexpr int BNB = 256;
+  constexpr int NT = 512;
+  extern __shared__ __attribute__((aligned(1024))) char dlds[];
+  if (p.zero_out) {  // every workgroup clears its share, with or without a tile
+    const int64_t n4 = p.zero_n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT)
+      ((float4*)p.zero_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < p.zero_n - n4 * 4) p.zero_out[n4 * 4 + threadIdx.x] = 0.f;
+  }
+  TileMap t;
+  if (!map_tile<MODE, 256, NT>(p, t)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, widx = wave & 3;
+  const int K = p.K, N = p.N, KW = p.kb_len;
+  const int kbeg_el = t.kbeg * BK;
+  const int nk = (t.nk * BK) / 64;       // 64-deep steps
+  const int nkw = KW / 64;              // B's steps (A may hold two terms per unit: wrap)
+  const int kbeg_st = kbeg_el / 64;
+  const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
+  const int64_t ebytes = (int64_t)N * KW * 2;
+  const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
+
+  // ---- DMA: wave widx of group 0 loads B tile rows widx*64 .. +64 (in
+  // MODE_GATEUP waves 0, 1 rows of W1, waves 2, 3 the same rows of W3), of
+  // group 1 the A tile rows widx*64 .. +64; instruction j fills 1 KiB = 8 rows.
+  const bool b_loader = grp == 0;
+  const bool w3 = (MODE == MODE_GATEUP) && b_loader && widx >= 2;
+  const void* bsrc = w3 ? (t.shared_e ? p.B1s : p.B1) : (t.shared_e ? p.B0s : p.B0);
+  const __amdgpu_buffer_rsrc_t rsW = uniform_rsrc(
+      b_loader ? (const char*)bsrc + eoff : (const char*)p.A, b_loader ? ebytes : p.A_bytes);
+  constexpr uint32_t kOobOff = 0x80000000u;
+  uint32_t voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = widx * 64 + j * 8 + lane / C::CPR;  // tile row, 0..255
+    const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
+    if (b_loader) {
+      const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+      voff[j] = n < N ? (uint32_t)((int64_t)n * KW * 2 + chunk * 16) : kOobOff;
+    } else {
+      const int m = t.m0 + r;
+      voff[j] = m < t.rows ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16)
+                           : kOobOff;
+    }
+  }
+  // activation instructions whose 8 rows all lie past the segment's end are
+  // not issued (a prefix of the wave's 8 is)
+  const int n_inst = b_loader ? 8
+                              : __builtin_amdgcn_readfirstlane(
+                                    max(0, min(8, (t.rows - t.m0 - widx * 64 + 7) / 8)));
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    char* dst = dlds + (kt & 1) * C::STAGE_BYTES + (b_loader ? C::TILE_BYTES : 0) +
+                widx * 64 * C::RB;
+    int kb = kbeg_st + kt;
+    kb = kb >= nkw ? kb - nkw : kb;
+    const int soff = __builtin_amdgcn_readfirstlane(b_loader ? kb * C::RBB : kt * C::RB);
+    static_for<8>([&](auto j) {
+      if (j < n_inst)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(dst + j * 1024), 16, voff[j], soff,
+                                                 0, 1);
+    });
+  };
+
+  // ---- the wave's tile
+  const int wm = wave & 1, wn = wave >> 1;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int swz = (frow / C::RPS) % C::CPR;  // fragment rows are 32-aligned + frow
+  const int arow0 = wm * 32;
+  int b_off[2];
+  b_off[0] = ((MODE == MODE_GATEUP) ? wn * 32 : wn * 64) * C::RB;
+  b_off[1] = ((MODE == MODE_GATEUP) ? BNB / 2 + wn * 32 : wn * 64 + 32) * C::RB;
+  const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
+  const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
+
+  if (nk <= 0) return;  // (every unit of the schedule has at least one step)
+  // prologue: steps 0 and 1 in flight, wait for step 0
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 1)
+    wait_vmcnt_dyn<8>(n_inst);
+  else
+    wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run = [&](auto NGc) __attribute__((always_inline)) {
+    constexpr int NG = decltype(NGc)::value;
+    constexpr int NGA = NG > 0 ? NG : 1;
+    f32x16 acc[NGA][2];
+#pragma unroll
+    for (int i = 0; i < NGA; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    bf16x8 fa[2][NGA], fb[2][2];
+    const int nsl = nk * 2;
+    if (grp == 1) bar();
+    for (int sl = 0; sl < nsl; ++sl) {
+      // read phase: slice sl (with, on even slices, the next step's DMA)
+      const int st = sl >> 1;
+      if ((sl & 1) == 0 && st >= 1 && st + 1 < nk) issue(st + 1);
+      if constexpr (NG > 0) {
+        const char* a = dlds + (st & 1) * C::STAGE_BYTES;
+        const char* b = a + C::TILE_BYTES;
+        static_for<2>([&](auto kk) {
+          const int co = ((((sl & 1) * 4 + kk * 2 + fhalf) ^ swz) * 16);
+#pragma unroll
+          for (int i = 0; i < NG; ++i)
+            fa[kk][i] = *(const bf16x8*)(a + (arow0 + i * 64 + frow) * C::RB + co);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) fb[kk][j] = *(const bf16x8*)(b + b_off[j] + frow * C::RB + co);
+        });
+      }
+      wait_lgkm0();
+      // activation loaders: their step (sl + 1) / 2 has landed before slice
+      // sl + 1 is read
+      if (grp == 1 && (sl & 1) && st + 1 < nk) wait_vmcnt<0>();
+      bar();
+      // compute phase
+      if constexpr (NG > 0) {
+        static_for<2>([&](auto kk) {
+#pragma unroll
+          for (int i = 0; i < NG; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              if (MODE == MODE_GATEUP)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+            }
+        });
+      }
+      // weight loaders: the same, at the end of their compute phase
+      if (grp == 0 && (sl & 1) && st + 1 < nk) wait_vmcnt<0>();
+      bar();
+    }
+    if (grp == 0) bar();
+    if constexpr (NG > 0) store_tile_pp<MODE, NG>(p, acc, t, arow0, n0, wn);
+  };
+  if (ng >= 4)
+    run(std::integral_constant<int, 4>{});
+  else if (ng == 3)
+    run(std::integral_constant<int, 3>{});
+  else if (ng == 2)
+    run(std::integral_constant<int, 2>{});
+  else if (ng == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
 }
 
 // Linear+bias experts in fp32 (the tutorial's nn.Linear(d, d) experts, §4.1).
@@ -1001,19 +1314,20 @@ inline unsigned sched_grid(const GemmParams& p) {
 // with few rows have little compute to hide the operand latency behind and
 // take smaller activation tiles, which leave LDS for more stages or a second
 // workgroup per CU.
-template <int MODE, int WQ, int KB, int NS, int BMA = 256>
+template <int MODE, int WQ, int KB, int NS, int BMA = 256, int PF = 0>
 hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
   using C = DmaCfg<KB, NS, wq_bits(WQ), BMA>;
-  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA>;
+  constexpr size_t kLds = C::LDS + (PF ? kPfSinkBytes : 0);
+  const void* kern = (const void*)grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA, PF>;
   static KernelSlots ks;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(ks.once[dev], [&] {
-    ks.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
-    if (ks.err[dev] == hipSuccess) ks.slots[dev] = xcd_slots(kern, C::LDS, dev);
+    ks.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (ks.err[dev] == hipSuccess) ks.slots[dev] = xcd_slots(kern, kLds, dev);
   });
   if (ks.err[dev] != hipSuccess) return ks.err[dev];
   const int slots = ks.slots[dev];
@@ -1026,7 +1340,7 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
     p.split_max = 1;
   // row tiles of BMA rows: sum_e ceil(rows_e / BMA) <= P_max / BMA + E (+ shared)
   p.mt_max = (int)((p.P_max + BMA - 1) / BMA + p.E + (p.has_shared ? (p.T + BMA - 1) / BMA : 0));
-  grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA><<<sched_grid(p), 256, C::LDS, st>>>(p);
+  grouped_gemm_dma_kernel<MODE, KB, NS, 1, WQ, BMA, PF><<<sched_grid(p), 256, kLds, st>>>(p);
   if (slab_mode && p.split_max > 1)
     // split tail tiles exist only with S >= 2 pieces, so rem <= slots / 2 of
     // them per XCD; bands past BMA rows hold nothing
@@ -1036,6 +1350,45 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+
+// The ping-pong kernel (bf16 weights, 256-row tiles): 512 threads, two
+// 64-deep stages of 64 KiB.
+template <int MODE>
+hipError_t launch_gemm_pp(const GemmParams& p0, hipStream_t st) {
+  if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
+  using C = DmaCfg<64, 2, 16, 256>;
+  constexpr size_t kLds = C::LDS;
+  const void* kern = (const void*)grouped_gemm_pp_kernel<MODE>;
+  static KernelSlots ks;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(ks.once[dev], [&] {
+    ks.err[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (ks.err[dev] == hipSuccess) {
+      int occ = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 512, kLds) != hipSuccess) occ = 1;
+      ks.slots[dev] = std::max(1, device_cus(dev) / kNumXcd) * std::max(1, occ);
+    }
+  });
+  if (ks.err[dev] != hipSuccess) return ks.err[dev];
+  const int slots = ks.slots[dev];
+  GemmParams p = p0;
+  p.kunit = 64 / BK;
+  p.slots = slots;
+  p.slab_piece = 256 * 256;
+  constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
+  if (slab_mode && (!p.tail_slab || (int64_t)kNumXcd * slots * p.slab_piece > p.slab_floats))
+    p.split_max = 1;
+  p.mt_max = (int)((p.P_max + 255) / 256 + p.E + (p.has_shared ? (p.T + 255) / 256 : 0));
+  grouped_gemm_pp_kernel<MODE><<<sched_grid(p), 512, kLds, st>>>(p);
+  if (slab_mode && p.split_max > 1)
+    tail_fixup_kernel<MODE, 256><<<(unsigned)(kNumXcd * std::max(1, slots / 2) * kFixBands), 256, 0,
+                                   st>>>(p);
+  return hipGetLastError();
+}
 
 // Runtime weight format and pipeline shape -> the kernel instantiation.
 template <int MODE>
@@ -1061,7 +1414,8 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
   if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
   if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
   if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 2>(p, st);
-  return launch_gemm_dma<MODE, WQ_BF16, 64, 2>(p, st);
+  if (MOE_GEMM_PP) return launch_gemm_pp<MODE>(p, st);
+  return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 256, MOE_GEMM_PF>(p, st);
 }
 
 }  // namespace

@@ -65,6 +65,9 @@
 #ifndef MOE_GEMM_PP
 #define MOE_GEMM_PP 1
 #endif
+#ifndef MOE_PP8_ROWS
+#define MOE_PP8_ROWS 256
+#endif
 
 namespace moe {
 namespace {
@@ -880,16 +883,25 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 // (transposed product): acc[i][0] / acc[i][1] hold gate / up rows wn*32 + R of
 // the weight tile, R = (r / 4) * 8 + (lane / 32) * 4 + r % 4, for activation
 // row arow0 + 64 i + lane % 32; DOWN*: acc[i][j] holds activation row
-// arow0 + 64 i + R, output column wn*64 + 32 j + lane % 32.
-template <int MODE, int NG>
+// arow0 + 64 i + R, output column wn*64 + 32 j + lane % 32.  Quantised
+// weights (QS): the per-128-output scales multiply the sums here.
+template <int MODE, int NG, bool QS>
 __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)[NG][2],
                                               const TileMap& t, int arow0, int n0, int wn) {
   const int lane = threadIdx.x & 63;
   const int ccol = lane & 31;
   const int rbase = (lane >> 5) * 4;
   const int N = p.N;
+  const int64_t sbase = t.shared_e ? 0 : (int64_t)t.e * (N / kFp8Group);
   if (MODE == MODE_GATEUP) {
     const int64_t hbase = t.shared_e ? p.P_max : (int64_t)t.seg;
+    // the wave's 32 hidden columns share one scale group
+    float sg = 1.f, su = 1.f;
+    if (QS) {
+      const int gi = (n0 + wn * 32) / kFp8Group;
+      sg = (t.shared_e ? p.sc0s : p.sc0 + sbase)[gi];
+      su = (t.shared_e ? p.sc1s : p.sc1 + sbase)[gi];
+    }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -902,22 +914,30 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
         if (n >= N) continue;
         if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
           float* sl = p.tail_slab + (int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0);
-          *(float4*)sl = make_float4(acc[i][0][q * 4], acc[i][0][q * 4 + 1], acc[i][0][q * 4 + 2],
-                                     acc[i][0][q * 4 + 3]);
-          *(float4*)(sl + 128) = make_float4(acc[i][1][q * 4], acc[i][1][q * 4 + 1],
-                                             acc[i][1][q * 4 + 2], acc[i][1][q * 4 + 3]);
+          *(float4*)sl = make_float4(acc[i][0][q * 4] * sg, acc[i][0][q * 4 + 1] * sg,
+                                     acc[i][0][q * 4 + 2] * sg, acc[i][0][q * 4 + 3] * sg);
+          *(float4*)(sl + 128) = make_float4(acc[i][1][q * 4] * su, acc[i][1][q * 4 + 1] * su,
+                                             acc[i][1][q * 4 + 2] * su, acc[i][1][q * 4 + 3] * su);
           continue;
         }
         float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float a = acc[i][0][q * 4 + r];
-          hv[r] = a / (1.f + __expf(-a)) * acc[i][1][q * 4 + r];
+          const float a = acc[i][0][q * 4 + r] * sg;
+          hv[r] = a / (1.f + __expf(-a)) * (acc[i][1][q * 4 + r] * su);
         }
         store_h4(hrow, n, N, hv, p.h_split);
       }
     }
   } else {
+    float sc[2] = {1.f, 1.f};
+    if (QS) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32;
+        sc[j] = n < N ? (t.shared_e ? p.sc0s : p.sc0 + sbase)[n / kFp8Group] : 0.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
 #pragma unroll
@@ -944,7 +964,7 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
           for (int j = 0; j < 2; ++j) {
             const int n = n0 + wn * 64 + j * 32 + ccol;
             if (n >= N) continue;
-            const float v = acc[i][j][q * 4 + r];
+            const float v = acc[i][j][q * 4 + r] * sc[j];
             if (MODE == MODE_DOWN)
               atomicAdd(&p.y[orow * N + n], wgt * v);
             else if (t.slab >= 0)
@@ -959,25 +979,30 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong kernel for bf16 weights: 256 x 256 tiles, 512 threads = 8 waves,
-// two per SIMD (wave w runs on SIMD w % 4).  Wave w computes 128 activation
-// rows (the 32-row granules (w & 1) + 2i) x 64 weight rows (quarter w >> 1;
-// in MODE_GATEUP 32 rows of W1 and the same 32 rows of W3).  Each wave
-// alternates a read phase (the 12 fragments of one 32-deep K slice, LDS ->
-// registers) and a compute phase (16 MFMAs 32x32x16 on them); waves 4..7 run
-// one phase behind waves 0..3, so on every SIMD one wave's MFMAs issue back to
-// back while the other's LDS reads are in flight.  A barrier separates the
-// phases.  Operands move global -> LDS by buffer_load ... lds in two 64-deep
-// stages (the XOR-swizzled row layout of DmaCfg): waves 0..3 fetch step u's
-// weight tile during their read of slice 2u - 2, waves 4..7 its activation
-// tile one phase later, and both wait for their own loads at the end of the
-// phase before slice 2u is first read.  Tile map, K split and the partial
-// tile slab are those of grouped_gemm_dma_kernel.
-template <int MODE>
+// Ping-pong kernel: 256 x 256 tiles, 512 threads = 8 waves, two per SIMD
+// (wave w runs on SIMD w % 4).  Wave w computes 128 activation rows (the
+// 32-row granules (w & 1) + 2i) x 64 weight rows (quarter w >> 1; in
+// MODE_GATEUP 32 rows of W1 and the same 32 rows of W3).  Each wave
+// alternates a read phase (the fragments of one 32-deep K slice, LDS ->
+// registers; 8-bit weight codes are widened exactly to bf16 here) and a
+// compute phase (16 MFMAs 32x32x16 on them); waves 4..7 run one phase behind
+// waves 0..3, so on every SIMD one wave's MFMAs issue back to back while the
+// other's LDS reads and conversions are in flight.  A barrier separates the
+// phases.  Operands move global -> LDS by buffer_load ... lds into NS stages
+// of 64-deep steps (the XOR-swizzled row layout of DmaCfg): waves 0..3 fetch
+// the weight tile of step s + NS - 1 during their read of slice 2s, waves
+// 4..7 its activation tile one phase later, and each waits for its own loads
+// of a step at the end of the phase before that step is first read.  Tile
+// map, K split and the partial-tile slab are those of grouped_gemm_dma_kernel.
+template <int MODE, int WQ, int NS>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
-  using C = DmaCfg<64, 2, 16, 256>;
+  static_assert(WQ == WQ_BF16 || WQ == WQ_FP8 || WQ == WQ_INT8, "bf16 or 8-bit weights");
+  constexpr bool QW = WQ != WQ_BF16;  // weight codes with scales
+  constexpr int WBITS = wq_bits(WQ);
+  using C = DmaCfg<64, NS, WBITS, 256>;
   constexpr int BNB = 256;
   constexpr int NT = 512;
+  constexpr int NIB = 64 / C::ROWS_PER_INST_B;  // B DMA instructions per wave and step
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
   if (p.zero_out) {  // every workgroup clears its share, with or without a tile
     const int64_t n4 = p.zero_n / 4;
@@ -997,12 +1022,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   const int nkw = KW / 64;              // B's steps (A may hold two terms per unit: wrap)
   const int kbeg_st = kbeg_el / 64;
   const int n0 = (MODE == MODE_GATEUP) ? t.ntile * (BNB / 2) : t.ntile * BNB;
-  const int64_t ebytes = (int64_t)N * KW * 2;
+  const int64_t ebytes = (int64_t)N * KW * WBITS / 8;
   const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
 
   // ---- DMA: wave widx of group 0 loads B tile rows widx*64 .. +64 (in
   // MODE_GATEUP waves 0, 1 rows of W1, waves 2, 3 the same rows of W3), of
-  // group 1 the A tile rows widx*64 .. +64; instruction j fills 1 KiB = 8 rows.
+  // group 1 the A tile rows widx*64 .. +64; an instruction fills 1 KiB.
   const bool b_loader = grp == 0;
   const bool w3 = (MODE == MODE_GATEUP) && b_loader && widx >= 2;
   const void* bsrc = w3 ? (t.shared_e ? p.B1s : p.B1) : (t.shared_e ? p.B0s : p.B0);
@@ -1012,12 +1037,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   uint32_t voff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = widx * 64 + j * 8 + lane / C::CPR;  // tile row, 0..255
-    const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
     if (b_loader) {
+      const int r = widx * 64 + j * C::ROWS_PER_INST_B + lane / C::CPRB;  // tile row, 0..255
+      const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
       const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
-      voff[j] = n < N ? (uint32_t)((int64_t)n * KW * 2 + chunk * 16) : kOobOff;
+      voff[j] = (j < NIB && n < N) ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
     } else {
+      const int r = widx * 64 + j * C::ROWS_PER_INST + lane / C::CPR;
+      const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
       const int m = t.m0 + r;
       voff[j] = m < t.rows ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16)
                            : kOobOff;
@@ -1025,12 +1052,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   }
   // activation instructions whose 8 rows all lie past the segment's end are
   // not issued (a prefix of the wave's 8 is)
-  const int n_inst = b_loader ? 8
+  const int n_inst = b_loader ? NIB
                               : __builtin_amdgcn_readfirstlane(
                                     max(0, min(8, (t.rows - t.m0 - widx * 64 + 7) / 8)));
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    char* dst = dlds + (kt & 1) * C::STAGE_BYTES + (b_loader ? C::TILE_BYTES : 0) +
-                widx * 64 * C::RB;
+    char* dst = dlds + (kt % NS) * C::STAGE_BYTES +
+                (b_loader ? C::TILE_BYTES + widx * 64 * C::RBB : widx * 64 * C::RB);
     int kb = kbeg_st + kt;
     kb = kb >= nkw ? kb - nkw : kb;
     const int soff = __builtin_amdgcn_readfirstlane(b_loader ? kb * C::RBB : kt * C::RB);
@@ -1040,26 +1067,36 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
                                                  0, 1);
     });
   };
+  // "every load of step u has landed": the loads of the later steps issued
+  // so far (up to step min(u + NS - 2, nk - 1)) may stay in flight
+  auto wait_step = [&](int u) __attribute__((always_inline)) {
+    const int later = min(u + NS - 2, nk - 1) - u;
+    if (NS == 2 || later <= 0)
+      wait_vmcnt<0>();
+    else if (b_loader)
+      wait_vmcnt_dyn<8 * (NS - 2)>(later * NIB);
+    else
+      wait_vmcnt_dyn<8 * (NS - 2)>(later * n_inst);
+  };
 
   // ---- the wave's tile
   const int wm = wave & 1, wn = wave >> 1;
   const int frow = lane & 31, fhalf = lane >> 5;
-  const int swz = (frow / C::RPS) % C::CPR;  // fragment rows are 32-aligned + frow
+  const int swz = (frow / C::RPS) % C::CPR;     // fragment rows are 32-aligned + frow
+  const int swzb = (frow / C::RPSB) % C::CPRB;
   const int arow0 = wm * 32;
-  int b_off[2];
-  b_off[0] = ((MODE == MODE_GATEUP) ? wn * 32 : wn * 64) * C::RB;
-  b_off[1] = ((MODE == MODE_GATEUP) ? BNB / 2 + wn * 32 : wn * 64 + 32) * C::RB;
+  int b_row[2];
+  b_row[0] = (MODE == MODE_GATEUP) ? wn * 32 + frow : wn * 64 + frow;
+  b_row[1] = (MODE == MODE_GATEUP) ? BNB / 2 + wn * 32 + frow : wn * 64 + 32 + frow;
   const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
   const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
 
   if (nk <= 0) return;  // (every unit of the schedule has at least one step)
-  // prologue: steps 0 and 1 in flight, wait for step 0
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 1)
-    wait_vmcnt_dyn<8>(n_inst);
-  else
-    wait_vmcnt<0>();
+  // prologue: steps 0 .. NS - 2 in flight, wait for step 0
+  static_for<NS - 1>([&](auto u) {
+    if (u < nk) issue(u);
+  });
+  wait_step(0);
   __builtin_amdgcn_s_barrier();
 
   auto bar = [&]() __attribute__((always_inline)) {
@@ -1078,28 +1115,52 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     bf16x8 fa[2][NGA], fb[2][2];
+    using BCode = std::conditional_t<QW, uint2, bf16x8>;
+    BCode fq[2][2];
     const int nsl = nk * 2;
+    int stage = 0;  // st % NS
     if (grp == 1) bar();
     for (int sl = 0; sl < nsl; ++sl) {
-      // read phase: slice sl (with, on even slices, the next step's DMA)
+      // read phase: slice sl (with, on even slices, the DMA of step st + NS - 1)
       const int st = sl >> 1;
-      if ((sl & 1) == 0 && st >= 1 && st + 1 < nk) issue(st + 1);
+      if ((sl & 1) == 0 && st + NS - 1 < nk) issue(st + NS - 1);
       if constexpr (NG > 0) {
-        const char* a = dlds + (st & 1) * C::STAGE_BYTES;
+        const char* a = dlds + stage * C::STAGE_BYTES;
         const char* b = a + C::TILE_BYTES;
         static_for<2>([&](auto kk) {
           const int co = ((((sl & 1) * 4 + kk * 2 + fhalf) ^ swz) * 16);
 #pragma unroll
           for (int i = 0; i < NG; ++i)
             fa[kk][i] = *(const bf16x8*)(a + (arow0 + i * 64 + frow) * C::RB + co);
+          if constexpr (!QW) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) fb[kk][j] = *(const bf16x8*)(b + b_off[j] + frow * C::RB + co);
+            for (int j = 0; j < 2; ++j) fq[kk][j] = *(const bf16x8*)(b + b_row[j] * C::RBB + co);
+          } else {
+            // the lane's 8 codes: K offset (sl & 1) * 32 + kk * 16 + fhalf * 8 of the step
+            const int bo = (sl & 1) * 32 + kk * 16 + fhalf * 8;
+            const int cb = (((bo >> 4) ^ swzb) << 4) + (bo & 15);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fq[kk][j] = *(const uint2*)(b + b_row[j] * C::RBB + cb);
+          }
         });
       }
       wait_lgkm0();
-      // activation loaders: their step (sl + 1) / 2 has landed before slice
-      // sl + 1 is read
-      if (grp == 1 && (sl & 1) && st + 1 < nk) wait_vmcnt<0>();
+      if constexpr (NG > 0) {
+        static_for<2>([&](auto kk) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (WQ == WQ_FP8)
+              fb[kk][j] = fp8x8_to_bf16x8(fq[kk][j]);
+            else if constexpr (WQ == WQ_INT8)
+              fb[kk][j] = int8x8_to_bf16x8(fq[kk][j]);
+            else
+              fb[kk][j] = fq[kk][j];
+          }
+        });
+      }
+      // activation loaders: their loads of step st + 1 have landed before
+      // slice sl + 1 = 2 (st + 1) is read
+      if (grp == 1 && (sl & 1) && st + 1 < nk) wait_step(st + 1);
       bar();
       // compute phase
       if constexpr (NG > 0) {
@@ -1116,11 +1177,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
         });
       }
       // weight loaders: the same, at the end of their compute phase
-      if (grp == 0 && (sl & 1) && st + 1 < nk) wait_vmcnt<0>();
+      if (grp == 0 && (sl & 1) && st + 1 < nk) wait_step(st + 1);
+      if (sl & 1) stage = stage + 1 == NS ? 0 : stage + 1;
       bar();
     }
     if (grp == 0) bar();
-    if constexpr (NG > 0) store_tile_pp<MODE, NG>(p, acc, t, arow0, n0, wn);
+    if constexpr (NG > 0) store_tile_pp<MODE, NG, QW>(p, acc, t, arow0, n0, wn);
   };
   if (ng >= 4)
     run(std::integral_constant<int, 4>{});
@@ -1352,14 +1414,14 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
 
 
 
-// The ping-pong kernel (bf16 weights, 256-row tiles): 512 threads, two
-// 64-deep stages of 64 KiB.
-template <int MODE>
+// The ping-pong kernel (256-row tiles): 512 threads, NS 64-deep stages
+// (bf16 weights: two of 64 KiB; 8-bit weights: three of 48 KiB).
+template <int MODE, int WQ, int NS>
 hipError_t launch_gemm_pp(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  using C = DmaCfg<64, 2, 16, 256>;
+  using C = DmaCfg<64, NS, wq_bits(WQ), 256>;
   constexpr size_t kLds = C::LDS;
-  const void* kern = (const void*)grouped_gemm_pp_kernel<MODE>;
+  const void* kern = (const void*)grouped_gemm_pp_kernel<MODE, WQ, NS>;
   static KernelSlots ks;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -1379,11 +1441,12 @@ hipError_t launch_gemm_pp(const GemmParams& p0, hipStream_t st) {
   p.kunit = 64 / BK;
   p.slots = slots;
   p.slab_piece = 256 * 256;
+  p.krot = 0;
   constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
   if (slab_mode && (!p.tail_slab || (int64_t)kNumXcd * slots * p.slab_piece > p.slab_floats))
     p.split_max = 1;
   p.mt_max = (int)((p.P_max + 255) / 256 + p.E + (p.has_shared ? (p.T + 255) / 256 : 0));
-  grouped_gemm_pp_kernel<MODE><<<sched_grid(p), 512, kLds, st>>>(p);
+  grouped_gemm_pp_kernel<MODE, WQ, NS><<<sched_grid(p), 512, kLds, st>>>(p);
   if (slab_mode && p.split_max > 1)
     tail_fixup_kernel<MODE, 256><<<(unsigned)(kNumXcd * std::max(1, slots / 2) * kFixBands), 256, 0,
                                    st>>>(p);
@@ -1411,10 +1474,17 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
     if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 32>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3, 64>(p, st);
   }
-  if (wq == WQ_FP8) return launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
-  if (wq == WQ_INT8) return launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
+  // 8-bit weights: the ping-pong kernel when experts fill whole 256-row
+  // tiles; with fewer rows its phases are short and their barriers dominate
+  // (measured on the 256-expert layer, about 128 rows per expert: fp8 6.41 ms
+  // with the four-wave kernel against 7.26 ms)
+  const bool pp8 = MOE_GEMM_PP && rows >= MOE_PP8_ROWS;
+  if (wq == WQ_FP8)
+    return pp8 ? launch_gemm_pp<MODE, WQ_FP8, 3>(p, st) : launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
+  if (wq == WQ_INT8)
+    return pp8 ? launch_gemm_pp<MODE, WQ_INT8, 3>(p, st) : launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
   if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 2>(p, st);
-  if (MOE_GEMM_PP) return launch_gemm_pp<MODE>(p, st);
+  if (MOE_GEMM_PP) return launch_gemm_pp<MODE, WQ_BF16, 2>(p, st);
   return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 256, MOE_GEMM_PF>(p, st);
 }
 

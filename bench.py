@@ -434,6 +434,15 @@ def main() -> int:
             "hbm_frac_over_step": wb / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "gbs_over_ffn_stages": wb / ((gu_ms + dn_ms) * 1e-3) / 1e9}
 
+    # ---- the one-time router packing the layer did at construction (outside
+    # moe_forward, so outside the timed steps), timed on its own
+    if H.layer.W_g_packed is not None:
+        pk = lambda: moe.moe_pack_router(H.layer.shape, H.W_g, H.layer.W_g_packed)  # noqa: E731
+        pk()
+        result["router_pack"] = {"bytes": int(H.layer.W_g_packed.numel()),
+                                 "us_once": time_steps(pk, 10) * 1e3,
+                                 "note": "moe_pack_router, once per layer, not in the timed steps"}
+
     # ---- online EPLB on the device: replicas + placement onto 8 devices from
     # this step's counts (still on the device), E/8 extra replicas
     D, extra = 8, max(1, cfg.E // 8)

@@ -143,6 +143,9 @@ typedef struct moe_shape {
                            both against W2 (h's rounding error about 2^-17 instead of
                            2^-9; twice the down projection's MFMA work and hidden-buffer
                            bytes) */
+  int32_t router_packed; /* 1: the W_g argument of moe_route / moe_forward is the packed
+                            router buffer written by moe_pack_router, not the fp32 [d, E]
+                            matrix (needs bf16 x and d % 32 == 0) */
 } moe_shape;
 
 /* Expert weights [device].  Unused members may be NULL. */
@@ -176,6 +179,25 @@ int moe_capacity(int64_t T, int32_t E, int32_t k, double cf);
  * Returns 0 for an invalid shape.  The workspace must be 256-byte aligned. */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
+/* Bytes of the packed router weights moe_pack_router writes for `shape` [host]:
+ * three bf16 planes [3][E_pad][d] (E_pad = E rounded up to a power of two, at
+ * least 16).  0 when the shape's router cannot use them (fp32 x, or d not a
+ * multiple of 32) or the shape is invalid. */
+size_t moe_router_packed_bytes(const moe_shape* shape);
+
+/* One-time packing of the router's gate weights (iopenshare §2.1 TopKGating,
+ * tutorial §4.1 gate Linear; the packed form is this library's): W_g [d, E]
+ * fp32 is split exactly into three bf16 parts, hi + mid + lo = W_g, stored
+ * transposed, which the MFMA router multiplies with the bf16 activations and
+ * sums in fp32 (the logits keep fp32 accuracy).  moe_route and moe_forward
+ * do this split on every call unless shape->router_packed is 1 and W_g points
+ * to this buffer.
+ *   W_g [device] fp32 [d, E]; packed [device] moe_router_packed_bytes(shape)
+ *   bytes, 16-byte aligned, owned by the caller; enqueued on `stream`.
+ * MOE_ERR_UNSUPPORTED when the shape's router does not take packed weights. */
+moe_status moe_pack_router(const moe_shape* shape, const float* W_g, void* packed,
+                           void* stream);
+
 /* Router, stage 1 (iopenshare §2.1 TopKGating; tutorial §3.1 and §4.1 table
  * steps 1-3).  logits = x W_g (+ b_g) in fp32; the k largest logits are kept
  * (slot 0 the largest, equal logits: the lower expert index first, -0 == +0);
@@ -186,7 +208,8 @@ size_t moe_workspace_bytes(const moe_shape* shape);
  * logit, each token keeps its topk_groups best groups (equal scores: the lower
  * group), and the top-k is taken among those groups' experts only; the
  * weights follow the same rule.
- *   x [device] [T, d] (act_dtype); W_g [device] [d, E] fp32; b_g [device] [E] or NULL;
+ *   x [device] [T, d] (act_dtype); W_g [device] [d, E] fp32 (or, with
+ *   shape->router_packed, moe_pack_router's buffer); b_g [device] [E] or NULL;
  *   logits [device] [T, E] fp32 output or NULL; topk_idx, topk_w [device] outputs;
  *   ws [device] workspace of moe_workspace_bytes(shape) bytes. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* W_g,

@@ -30,7 +30,8 @@ COMBINE_AUTO, COMBINE_GROUPED, COMBINE_FUSED = 0, 1, 2
 COMBINE = {"auto": COMBINE_AUTO, "grouped": COMBINE_GROUPED, "fused": COMBINE_FUSED}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP"}
 
-EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_route_from_logits",
+EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_router_packed_bytes", "moe_pack_router",
+           "moe_route", "moe_route_from_logits",
            "moe_reroute", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_forward_noalloc",
            "moe_load_imbalance", "moe_lpt_pack", "moe_eplb_plan", "moe_timing_enable",
@@ -52,7 +53,7 @@ class Shape(ctypes.Structure):
                 ("has_shared", ctypes.c_int32), ("overflow", ctypes.c_int32),
                 ("reroute_rounds", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("combine", ctypes.c_int32),
-                ("hidden_split", ctypes.c_int32)]
+                ("hidden_split", ctypes.c_int32), ("router_packed", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -67,6 +68,10 @@ _lib.moe_capacity.restype = ctypes.c_int
 _lib.moe_capacity.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
 _lib.moe_workspace_bytes.restype = ctypes.c_size_t
 _lib.moe_workspace_bytes.argtypes = [_P(Shape)]
+_lib.moe_router_packed_bytes.restype = ctypes.c_size_t
+_lib.moe_router_packed_bytes.argtypes = [_P(Shape)]
+_lib.moe_pack_router.restype = ctypes.c_int
+_lib.moe_pack_router.argtypes = [_P(Shape), _vp, _vp, _vp]
 _lib.moe_route.restype = ctypes.c_int
 _lib.moe_route.argtypes = [_P(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_route_from_logits.restype = ctypes.c_int
@@ -126,11 +131,13 @@ def _check(st):
 
 def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=DT_BF16,
                kind=SWIGLU, has_shared=False, overflow=OVERFLOW_DROP, reroute_rounds=0,
-               n_groups=0, topk_groups=0, combine=COMBINE_AUTO, hidden_split=False) -> Shape:
+               n_groups=0, topk_groups=0, combine=COMBINE_AUTO, hidden_split=False,
+               router_packed=False) -> Shape:
     """overflow: OVERFLOW_* or its name ("drop", "reroute", "shared").
     n_groups / topk_groups: group-limited routing (0 = off).
     combine: COMBINE_* or its name ("auto", "grouped", "fused").
-    hidden_split: keep the SwiGLU hidden activation as two bf16 terms."""
+    hidden_split: keep the SwiGLU hidden activation as two bf16 terms.
+    router_packed: W_g arguments are moe_pack_router's buffer."""
     if isinstance(overflow, str):
         overflow = OVERFLOW[overflow]
     if isinstance(combine, str):
@@ -138,7 +145,7 @@ def make_shape(T, d, E, top_k, d_ff=0, capacity=-1, act_dtype=DT_BF16, w_dtype=D
     return Shape(int(T), int(d), int(E), int(top_k), int(d_ff), int(capacity), int(act_dtype),
                  int(w_dtype), int(kind), int(bool(has_shared)), int(overflow),
                  int(reroute_rounds), int(n_groups), int(topk_groups), int(combine),
-                 int(bool(hidden_split)))
+                 int(bool(hidden_split)), int(bool(router_packed)))
 
 
 def make_weights(**tensors) -> Weights:
@@ -198,6 +205,14 @@ def workspace(shape: Shape, device="cuda") -> torch.Tensor:
     if n == 0:
         raise MoEError(1, moe_last_error() or "invalid shape")
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_router_packed_bytes(shape: Shape) -> int:
+    return int(_lib.moe_router_packed_bytes(ctypes.byref(shape)))
+
+
+def moe_pack_router(shape, W_g, packed, stream=None):
+    _check(_lib.moe_pack_router(ctypes.byref(shape), _ptr(W_g), _ptr(packed), _stream(stream)))
 
 
 def moe_route(shape, x, W_g, b_g, logits, topk_idx, topk_w, ws, stream=None):

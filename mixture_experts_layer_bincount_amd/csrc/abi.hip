@@ -52,6 +52,10 @@ moe_status check_shape(const moe_shape* s, bool need_ffn) {
     return fail(MOE_ERR_INVALID, "reroute_rounds=%d must be in [0, 1024]", s->reroute_rounds);
   if (s->overflow == MOE_OVERFLOW_SHARED && !s->has_shared)
     return fail(MOE_ERR_INVALID, "overflow to the shared expert needs has_shared");
+  if (s->router_packed < 0 || s->router_packed > 1)
+    return fail(MOE_ERR_INVALID, "router_packed=%d must be 0 or 1", s->router_packed);
+  if (s->router_packed && !router_mfma_epad(*s))
+    return fail(MOE_ERR_UNSUPPORTED, "packed router weights need bf16 x and d %% 32 == 0");
   if (s->hidden_split < 0 || s->hidden_split > 1)
     return fail(MOE_ERR_INVALID, "hidden_split=%d must be 0 or 1", s->hidden_split);
   if (s->combine < MOE_COMBINE_AUTO || s->combine > MOE_COMBINE_FUSED)
@@ -223,7 +227,7 @@ WsLayout ws_layout(const moe_shape& s) {
   L.off_partial = off;
   off = align256(off + (size_t)L.router_splits * s.T * s.E * sizeof(float));
   L.off_wsplit = off;
-  off = align256(off + router_split_bytes(s));
+  if (!s.router_packed) off = align256(off + router_split_bytes(s));
   L.off_chunk_hist = off;
   off = align256(off + (size_t)L.nchunks * s.E * sizeof(int32_t));
   L.off_chunk_base = off;
@@ -292,6 +296,20 @@ int moe_capacity(int64_t T, int32_t E, int32_t k, double cf) {
   const double c = ceil((cf * (double)(T * (int64_t)k)) / (double)E);
   if (c > 2147483647.0) return 2147483647;
   return (int)c;
+}
+
+size_t moe_router_packed_bytes(const moe_shape* shape) {
+  if (check_shape(shape, false) != MOE_OK) return 0;
+  return router_split_bytes(*shape);
+}
+
+moe_status moe_pack_router(const moe_shape* shape, const float* W_g, void* packed, void* stream) {
+  MOE_TRY(check_shape(shape, false));
+  if (!router_mfma_epad(*shape))
+    return fail(MOE_ERR_UNSUPPORTED, "this router takes no packed weights (fp32 x or d %% 32 != 0)");
+  MOE_TRY(check_ptr(W_g, "W_g"));
+  MOE_TRY(check_ptr(packed, "packed", 16));
+  return hip_status(launch_router_pack(*shape, W_g, packed, (hipStream_t)stream), "router pack");
 }
 
 size_t moe_workspace_bytes(const moe_shape* shape) {

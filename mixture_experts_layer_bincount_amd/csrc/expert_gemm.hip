@@ -68,6 +68,12 @@
 #ifndef MOE_PP8_ROWS
 #define MOE_PP8_ROWS 256
 #endif
+#ifndef MOE_DECODE_PF
+#define MOE_DECODE_PF 0
+#endif
+#ifndef MOE_DECODE_GU_SPLIT
+#define MOE_DECODE_GU_SPLIT 0
+#endif
 
 namespace moe {
 namespace {
@@ -527,17 +533,17 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-// L2 prefetch (PF = 1): when a workgroup issues the DMA of K step s, it also
-// touches every 128-byte line of step s + 1 of its A and B rows with one
-// 4-byte DMA per row into a sink in LDS that nothing reads, so those lines
-// are on their way to L2 a step before their DMA and that DMA hits L2.  A
-// 64-deep step of a row is exactly one line, so 512 rows take 8 instructions
-// (2 per wave) and 2 KiB of sink.
+// L2 prefetch (PF = d > 0): when a workgroup issues the DMA of K step s, it
+// also touches every 128-byte line of step s + d of its weight rows (and, in
+// 256-row tiles, of its activation rows) with one 4-byte DMA per row into a
+// sink in LDS that nothing reads, so those lines are on their way to L2 d
+// steps before their DMA.  A 64-deep bf16 step of a row is exactly one line,
+// so 128 rows take 2 instructions per wave, and the sink is 2 KiB.
 constexpr int kPfSinkBytes = 2048;
 
 template <int MODE, int KB, int NS, int MOE_AUX, int WQ, int BMA, int PF = 0>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) {
-  static_assert(!PF || (KB * 2 == 128 && BMA == 256 && NS == 2), "prefetch: 64-deep bf16 steps, 256-row tiles");
+  static_assert(!PF || (KB * 2 == 128 && WQ == WQ_BF16 && NS == 2), "prefetch: 64-deep bf16 steps, two stages");
   constexpr bool FP8 = WQ != WQ_BF16;  // quantised weight codes with scales
   constexpr int WBITS = wq_bits(WQ);
   using C = DmaCfg<KB, NS, WBITS, BMA>;
@@ -601,8 +607,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       voff[j] = n < N ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
     }
   });
-  // prefetch rows: A waves their 128 activation rows, B waves their 128 weight
-  // rows, lane + 64 j for j = 0, 1
+  // prefetch rows: B waves their 128 weight rows, A waves (256-row tiles
+  // only) their 128 activation rows, lane + 64 j for j = 0, 1
+  constexpr bool kPfA = BMA == 256;
+  const bool has_pf = PF != 0 && (!a_wave || kPfA);
   uint32_t pfoff[2] = {kOobOff, kOobOff};
   if constexpr (PF != 0) {
 #pragma unroll
@@ -660,10 +668,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       });
     }
     if constexpr (PF != 0) {
-      // the next step's lines (issued after this step's DMA, so waiting for
-      // this step leaves these two in flight)
-      if (kt + 1 < nk) {
-        const int kq = kt + 1 + krot < nk ? kt + 1 + krot : kt + 1 + krot - nk;
+      // the lines of step kt + PF (issued after this step's DMA, so waiting
+      // for this step leaves these two in flight)
+      if (has_pf && kt + PF < nk) {
+        const int kq = kt + PF + krot < nk ? kt + PF + krot : kt + PF + krot - nk;
         int kbq = kbeg_st + kq;
         kbq = kbq >= nkw ? kbq - nkw : kbq;
         const int spf = __builtin_amdgcn_readfirstlane(a_wave ? kq * C::RB : kbq * C::RBB);
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     // steady state: the NS - 2 later steps may stay in flight; near the end
     // (fewer issued) wait for everything.  With the prefetch the two touches
     // of step t + 1, issued after step t's DMA, may stay in flight.
-    if (PF != 0 && t + 1 < nk)
+    if (PF != 0 && has_pf && t + PF < nk)
       wait_vmcnt<2>();
     else if (t + NS - 2 <= nk - 1)
       wait_steps(std::integral_constant<int, NS - 2>{});
@@ -827,7 +835,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     static_for<NS - 1>([&](auto s) {
       if (s < nk) issue(s, s);
     });
-    if (PF != 0 && nk > 1)
+    if (PF != 0 && has_pf && PF < nk)
       wait_vmcnt<2>();
     else if (NS - 2 >= 2 && nk > 2)
       wait_steps(std::integral_constant<int, 2>{});
@@ -1471,7 +1479,7 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
     // bf16 weights at 16 or fewer rows per expert: 32-row tiles with two
     // 64-deep stages, two workgroups per CU (decode at 16 rows per expert
     // 0.576 -> 0.542 ms)
-    if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 32>(p, st);
+    if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 32, MOE_DECODE_PF>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3, 64>(p, st);
   }
   // 8-bit weights: the ping-pong kernel when experts fill whole 256-row
@@ -1591,6 +1599,7 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // tail tiles split over K through the slab + fixup (SwiGLU needs whole
   // sums), for long K loops only, as in the down projection
   g.split_max = s.d >= 4096 ? std::max(1, s.d / BK / 8) : 1;
+  if (!MOE_DECODE_GU_SPLIT && L.P_max / s.E <= 32) g.split_max = 1;
   // few rows per expert (decode-sized batches): smaller activation tiles and
   // deeper weight pipelines (launch_gemm; slower at 128 rows and more)
   const int64_t rows_avg = L.P_max / s.E;

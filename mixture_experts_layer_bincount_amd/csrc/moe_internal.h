@@ -96,6 +96,9 @@ int router_splits_for(const moe_shape& s);
 // the fp32-activation router runs instead (it handles up to 256 experts).
 int router_mfma_epad(const moe_shape& s);
 size_t router_split_bytes(const moe_shape& s);
+// The MFMA router's split gate planes [3][E_pad][d] bf16 from W_g [d, E] fp32.
+hipError_t launch_router_pack(const moe_shape& s, const float* W_g, void* packed, hipStream_t st);
+// W_g: the fp32 gate, or (s.router_packed) the packed planes.
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
                               float* partial, int splits, void* split_ws, hipStream_t st);
 // cand (optional): the selection continued to KR experts per token, cand[t,

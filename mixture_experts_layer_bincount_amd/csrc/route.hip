@@ -375,14 +375,25 @@ int router_splits_for(const moe_shape& s) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(kmax, (512 + mt - 1) / std::max<int64_t>(mt, 1)));
 }
 
+hipError_t launch_router_pack(const moe_shape& s, const float* W_g, void* packed, hipStream_t st) {
+  const int ep = router_mfma_epad(s);
+  if (!ep) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)ep * s.d;
+  router_split_kernel<<<(unsigned)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, st>>>(
+      W_g, s.d, s.E, ep, (uint16_t*)packed);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* W_g,
                               float* partial, int splits, void* split_ws, hipStream_t st) {
   const int ep = router_mfma_epad(s);
   if (ep) {
-    uint16_t* Wp = (uint16_t*)split_ws;
-    const int64_t n = (int64_t)ep * s.d;
-    router_split_kernel<<<(unsigned)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, st>>>(
-        W_g, s.d, s.E, ep, Wp);
+    // the split planes: packed once by the caller (moe_pack_router), or here
+    const uint16_t* Wp = s.router_packed ? (const uint16_t*)W_g : (const uint16_t*)split_ws;
+    if (!s.router_packed) {
+      const hipError_t e = launch_router_pack(s, W_g, split_ws, st);
+      if (e != hipSuccess) return e;
+    }
     const int ksteps = s.d / 32;
     const int per = (ksteps + splits - 1) / splits;
     dim3 grid((unsigned)((s.T + 255) / 256), (unsigned)splits, (unsigned)router_eblocks(ep));

@@ -111,7 +111,8 @@ def gpu_logits(layer, dev) -> np.ndarray:
     logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
     idx = torch.empty((s.T, s.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((s.T, s.top_k), dtype=torch.float32, device="cuda")
-    moe.moe_route(s, dev["x"], dev["W_g"], dev["b_g"], logits, idx, w, moe.workspace(s))
+    W_g = layer.W_g_packed if layer.W_g_packed is not None else dev["W_g"]
+    moe.moe_route(s, dev["x"], W_g, dev["b_g"], logits, idx, w, moe.workspace(s))
     torch.cuda.synchronize()
     return logits.cpu().numpy()
 

@@ -146,6 +146,26 @@ def test_workspace_follows_the_combine_form(moe, T):
     assert fused == moe.moe_workspace_bytes(moe.make_shape(T, 4096, 8, 2, 14336, combine="fused"))
 
 
+def test_router_packing_sizes_and_validation(moe):
+    """Packed router planes: 3 x E_pad x d bf16 (E_pad the power of two >= max(E, 16));
+    none for fp32 activations or d not a multiple of 32; a packed shape needs
+    no split planes in its workspace."""
+    assert moe.moe_router_packed_bytes(moe.make_shape(64, 4096, 8, 2, 14336)) == 3 * 16 * 4096 * 2
+    assert moe.moe_router_packed_bytes(moe.make_shape(64, 7168, 256, 8, 2048)) == 3 * 256 * 7168 * 2
+    assert moe.moe_router_packed_bytes(moe.make_shape(64, 7168, 257, 8, 2048)) == 3 * 512 * 7168 * 2
+    assert moe.moe_router_packed_bytes(moe.make_shape(64, 8, 4, 2, 0, -1, 0, 0, 0)) == 0
+    assert moe.moe_router_packed_bytes(moe.make_shape(64, 4104, 8, 2, 128)) == 0
+    plain = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408))
+    packed = moe.moe_workspace_bytes(moe.make_shape(4096, 4096, 64, 2, 1408, router_packed=True))
+    assert plain - packed >= 3 * 64 * 4096 * 2
+    with pytest.raises(moe.MoEError, match="packed"):
+        moe.moe_pack_router(moe.make_shape(64, 8, 4, 2, 0, -1, 0, 0, 0), 256, 256, stream=0)
+    s = moe.make_shape(16, 8, 4, 2, 0, -1, 0, 0, 0, router_packed=True)
+    with pytest.raises(moe.MoEError, match="packed"):
+        moe.moe_forward(s, 256, 256, None, moe.make_weights(W=256, b=256), 256, 256, 256, 256,
+                        256, 256, stream=0)
+
+
 def test_workspace_covers_rerouting(moe):
     """The re-routing state grows with the rounds: k more ranked candidates
     per token and round, up to E."""

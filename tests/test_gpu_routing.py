@@ -175,3 +175,32 @@ def test_group_limited_route_hand_worked(moe):
         torch.cuda.synchronize()
         assert idx.cpu().numpy()[0].tolist() == c["expected_idx"], c["name"]
 
+
+
+@pytest.mark.parametrize("T,d,E", [(64, 4096, 8), (300, 512, 64), (129, 7168, 256)])
+def test_packed_router_weights(moe, T, d, E):
+    """moe_pack_router's split planes, given to moe_route with router_packed,
+    give bit for bit the logits and routing of the fp32 gate split on every
+    call; moe_forward with them equals moe_forward without."""
+    from moe_synth import Workload, custom_config
+    from moe_synth.device import upload
+    cfg = custom_config(T, d, E, 2, 128, seed=T + E)
+    wl = Workload(cfg)
+    dev = upload(wl)
+    s0 = moe.make_shape(T, d, E, 2, 128)
+    s1 = moe.make_shape(T, d, E, 2, 128, router_packed=True)
+    packed = torch.empty(moe.moe_router_packed_bytes(s0), dtype=torch.uint8, device="cuda")
+    assert packed.numel() == 3 * max(16, 1 << (E - 1).bit_length()) * d * 2
+    moe.moe_pack_router(s0, dev["W_g"], packed)
+    outs = []
+    for s, W in ((s0, dev["W_g"]), (s1, packed)):
+        logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, 2), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+        moe.moe_route(s, dev["x"], W, None, logits, idx, w, moe.workspace(s))
+        torch.cuda.synchronize()
+        outs.append((logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    lg = oracle.router_logits(wl.x(), wl.W_g())
+    assert np.abs(outs[0][0] - lg).max() <= 1e-4 * max(1.0, np.abs(lg).max())

@@ -28,7 +28,8 @@ def _noalloc(moe, layer, dev):
     w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
     counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
     offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
-    moe.moe_forward_noalloc(s, dev["x"], dev["W_g"], dev["b_g"], layer.weights, y, idx, w,
+    W_g = layer.W_g_packed if layer.W_g_packed is not None else dev["W_g"]
+    moe.moe_forward_noalloc(s, dev["x"], W_g, dev["b_g"], layer.weights, y, idx, w,
                             counts, offsets)
     torch.cuda.synchronize()
     return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy(), w=w.cpu().numpy(),

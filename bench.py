@@ -73,11 +73,12 @@ def _blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def _traffic_from_profile(kernel_src: str, key: str):
+def _traffic_from_profile(kernel_src: str, key: str, workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None when the kernel source changed since."""
+    counter summary of the Mixtral-shaped workload, or None for another
+    workload or when the kernel source changed since."""
     path = os.path.join(ROOT, "profiles", "gate_up_swiglu_mixtral_counters.json")
-    if not os.path.exists(path):
+    if workload != "mixtral" or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -189,6 +190,41 @@ def weight_bytes(cfg, n_experts: int) -> int:
     return n_experts * per
 
 
+def gemm_kernel(cfg, cap: int, stage: str = "gate_up") -> str:
+    """The expert GEMM kernel the library launches for one stage ("gate_up"
+    or "down") of this workload.  The choice follows the average rows per
+    expert, P_max / E with P_max = min(T k, E C): up to 32 rows the four-wave
+    kernel with decode-sized activation tiles; otherwise the eight-wave
+    ping-pong kernel for bf16 weights and for 8-bit weights from 256 rows
+    up, its 128 x 512 tiles for the down projection of 8-bit weights with
+    fewer rows; the four-wave kernel with 256-row tiles for int4 and for the
+    gate/up projection of 8-bit weights with fewer rows."""
+    if cfg.kind != "swiglu":
+        return "linear_bias_kernel"
+    A = cfg.T * cfg.k
+    rows = (A if cap < 0 else min(A, cfg.E * cap)) // cfg.E
+    if rows <= 32:
+        return "grouped_gemm_dma_kernel (decode-sized tiles)"
+    if cfg.w == "bf16" or (cfg.w in ("fp8_e4m3", "int8") and rows >= 256):
+        return "grouped_gemm_pp_kernel"
+    if cfg.w in ("fp8_e4m3", "int8") and stage == "down":
+        return "grouped_gemm_pp_kernel (128 x 512 tiles)"
+    return "grouped_gemm_dma_kernel"
+
+
+def gate_up_bytes(cfg, kept_rows) -> int:
+    """Algorithmic bytes of the gate/up launch: W1 and W3 of the experts it
+    touches (codes and scales in the workload's format, the shared expert
+    included), the gathered x rows read once, H written once."""
+    wbits = {"bf16": 16, "fp8_e4m3": 8, "int8": 8, "int4": 4}[cfg.w]
+    n = sum(1 for v in kept_rows if v > 0) + (1 if cfg.shared else 0)
+    w = n * 2 * cfg.d * cfg.d_ff * wbits // 8
+    if wbits < 16:
+        w += n * 2 * (cfg.d_ff // 128) * 4
+    rows = int(sum(kept_rows)) + (cfg.T if cfg.shared else 0)
+    return w + rows * cfg.d * 2 + rows * cfg.d_ff * 2 * (2 if cfg.hidden_split else 1)
+
+
 def roofline_floor(cfg, kept_rows, kept: int) -> dict:
     """The binding floor of one step: max(MFMA time of the expert FLOPs at
     2.5 PFLOP/s, HBM time of the touched weights + x read once + y written
@@ -275,7 +311,9 @@ def sub_record(name: str, steps: int, warmup: int, parity: bool) -> dict:
                       "expert": c.kind, "weights": c.w, "shared": c.shared,
                       "capacity": L.cap, "hidden_split": c.hidden_split},
            "steps": steps, "ms_per_step": ms, "tokens_per_s": c.T / (ms * 1e-3),
-           "kept_assignments": kept, **floor,
+           "kept_assignments": kept,
+           "gemm_kernels": {"gate_up": gemm_kernel(c, L.cap), "down": gemm_kernel(c, L.cap, "down")},
+           **floor,
            "frac": floor["floor_ms"] / ms,
            "tflops": floor["ffn_flops"] / (ms * 1e-3) / 1e12,
            "hbm_gbs_over_step": floor["hbm_bytes"] / (ms * 1e-3) / 1e9}
@@ -376,14 +414,15 @@ def main() -> int:
     kept = int(sum(kept_rows))
     counts = H.layer.counts.cpu().tolist()
     y_gpu = H.layer.y.cpu().numpy()
-    flops_gate_up = 2.0 * kept * cfg.d * 2 * cfg.d_ff
-    flops_down = 2.0 * kept * cfg.d_ff * cfg.d
+    rows_gu = kept + (cfg.T if cfg.shared else 0)  # the shared expert runs over every token
+    flops_gate_up = 2.0 * rows_gu * cfg.d * 2 * cfg.d_ff
+    flops_down = 2.0 * rows_gu * cfg.d_ff * cfg.d
     flops_ffn = ffn_flops(cfg, kept)
     gu_ms = stage_ms["gate_up_swiglu"] / max(calls, 1)
     dn_ms = stage_ms["down_combine"] / max(calls, 1)
     achieved = flops_gate_up / (gu_ms * 1e-3) / 1e12
     gemm_src = os.path.join(ROOT, "mixture_experts_layer_bincount_amd", "csrc", "expert_gemm.hip")
-    traffic = _traffic_from_profile(gemm_src, "hbm_bytes_per_launch")
+    traffic = _traffic_from_profile(gemm_src, "hbm_bytes_per_launch", cfg.name)
     stages = {k: round(v / max(calls, 1), 4) for k, v in stage_ms.items()}
 
     result = {
@@ -409,11 +448,11 @@ def main() -> int:
         "stage_ms": stages,
         "ms_per_step_stage_timed": ms_instrumented,
         "counts": counts,
-        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (grouped_gemm_dma_kernel<GATEUP>)",
+        "roofline": {"kernel": f"grouped gate/up GEMM + SwiGLU ({gemm_kernel(cfg, H.cap)}<GATEUP>)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "algorithmic_per_launch": f"{flops_gate_up:.4e} FLOP = 2*{kept} rows*"
+                     "algorithmic_per_launch": f"{flops_gate_up:.4e} FLOP = 2*{rows_gu} rows*"
                                                f"{cfg.d}*2*{cfg.d_ff}",
                      "avg_launch_ms": gu_ms,
                      "timing": f"HIP events on the launch stream around the launch, "
@@ -422,6 +461,18 @@ def main() -> int:
                                       "tflops": flops_down / (dn_ms * 1e-3) / 1e12}},
         "load_stats": load_stats(moe, counts, kept_rows),
     }
+    # a workload whose binding floor is the HBM (decode-sized batches, the
+    # 256-expert layer): the gate/up launch's algorithmic bytes per second
+    # against 8 TB/s
+    floor = roofline_floor(cfg, kept_rows, kept) if cfg.kind == "swiglu" else None
+    if floor and floor["bound"] == "hbm":
+        gb = gate_up_bytes(cfg, kept_rows)
+        r = result["roofline"]
+        r.update({"bound": "hbm", "achieved": gb / (gu_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": gb / (gu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "algorithmic_per_launch": f"{gb:.4e} B = W1 + W3 of the touched experts "
+                                            f"+ {rows_gu} gathered x rows + H",
+                  "tflops": achieved})
 
     # ---- weight stream: the bytes of the experts this step touched (codes
     # and scales in the workload's weight format, the shared expert included)

@@ -15,11 +15,15 @@
 // A shared expert (iopenshare §1.4: always-active experts) is expert index E
 // with T rows, row t = token t, weight 1, hidden rows P_max .. P_max + T.
 //
-// Workgroup tile: 256 activation rows x 256 weight rows, K in steps of 64;
-// 256 threads = 4 waves of 128 x 128 (4 x 4 MFMA tiles of 32x32, 256 fp32
-// accumulators per lane).  Decode-sized batches (32 or fewer rows per expert
-// on average) use 64- or 32-row activation tiles instead, so two workgroups
-// share a CU.  A wave's activation rows are the 32-row granules
+// Two kernels.  The ping-pong kernel (grouped_gemm_pp_kernel, described at
+// its definition) takes bf16 weights and, for experts of 256 or more rows,
+// 8-bit weights on 256 x 256 tiles with 8 waves; the down projection of
+// 8-bit weights at 33..255 rows per expert takes its 128 x 512 tiles.  The
+// four-wave kernel (grouped_gemm_dma_kernel) takes the rest: workgroup tile
+// 256 activation rows x 256 weight rows, K in steps of 64; 256 threads = 4
+// waves of 128 x 128 (4 x 4 MFMA tiles of 32x32, 256 fp32 accumulators per
+// lane).  Decode-sized batches (32 or fewer rows per expert on average) use
+// 64- or 32-row activation tiles instead, so two workgroups share a CU.  A wave's activation rows are the 32-row granules
 // wm, wm + 2, wm + 4, wm + 6 of the tile, and it runs only the granules that
 // hold rows of the segment (partial tiles cost in proportion to their rows).
 // In MODE_GATEUP a wave's 128 weight rows are 64 rows of W1 and the same 64
@@ -67,6 +71,15 @@
 #endif
 #ifndef MOE_PP8_ROWS
 #define MOE_PP8_ROWS 256
+#endif
+#ifndef MOE_PP8_WIDE
+#define MOE_PP8_WIDE 6  // bit (1 << MODE): the launches that take 128 x 512 tiles
+#endif
+#ifndef MOE_PP_KROT
+#define MOE_PP_KROT 1
+#endif
+#ifndef MOE_DECODE_NS
+#define MOE_DECODE_NS 2
 #endif
 #ifndef MOE_DECODE_PF
 #define MOE_DECODE_PF 0
@@ -424,7 +437,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 constexpr int DMA_BM = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int KB, int NS, int WBITS, int BMA = 256>
+template <int KB, int NS, int WBITS, int BMA = 256, int BNT = 256>
 struct DmaCfg {
   // activation (A) tile: 256 rows of KB bf16
   static constexpr int RB = KB * 2;                 // bytes per A row and stage
@@ -433,18 +446,21 @@ struct DmaCfg {
   static constexpr int ROWS_PER_INST = 1024 / RB;   // A rows one wave-level DMA fills
   static constexpr int NI = BMA / 2 / ROWS_PER_INST;  // A DMA instructions per wave and stage
   static constexpr int TILE_BYTES = BMA * RB;         // the A tile (BMA activation rows)
-  // weight (B) tile: 256 rows of KB weights of WBITS bits (16 bf16, 8 or 4)
+  // weight (B) tile: BNT rows (256, or 512 under 128-row activation tiles)
+  // of KB weights of WBITS bits (16 bf16, 8 or 4)
   static constexpr int RBB = KB * WBITS / 8;         // bytes per B row and stage
   static constexpr int CPRB = RBB / 16;
   static constexpr int RPSB = 256 / RBB;
   static constexpr int ROWS_PER_INST_B = 1024 / RBB;
   static constexpr int NIB = 128 / ROWS_PER_INST_B; // B DMA instructions per wave and stage
-  static constexpr int B_TILE_BYTES = 256 * RBB;
+  static constexpr int B_TILE_BYTES = BNT * RBB;
   static constexpr int STAGE_BYTES = TILE_BYTES + B_TILE_BYTES;
   static constexpr int NI_MAX = NI > NIB ? NI : NIB;
   static constexpr size_t LDS = (size_t)NS * STAGE_BYTES;
   static_assert(KB % 32 == 0 && NS >= 2 && NS <= 4 && RBB >= 16, "DMA pipeline shape");
-  static_assert((BMA == 256 || BMA == 64 || BMA == 32) && NI >= 1, "activation tile rows");
+  static_assert((BMA == 256 || BMA == 128 || BMA == 64 || BMA == 32) && NI >= 1,
+                "activation tile rows");
+  static_assert(BNT == 256 || (BNT == 512 && BMA == 128), "weight tile rows");
   static_assert(LDS <= 150 * 1024, "LDS budget (with the static tile-map arrays)");
 };
 
@@ -887,13 +903,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 
 
 // Epilogue of the ping-pong kernel: the wave's NG granules (activation rows
-// arow0 + 64 i + 0..31) x its two 32-row weight tiles.  MODE_GATEUP
+// arow0 + RS i + 0..31) x its two 32-row weight tiles.  MODE_GATEUP
 // (transposed product): acc[i][0] / acc[i][1] hold gate / up rows wn*32 + R of
 // the weight tile, R = (r / 4) * 8 + (lane / 32) * 4 + r % 4, for activation
-// row arow0 + 64 i + lane % 32; DOWN*: acc[i][j] holds activation row
-// arow0 + 64 i + R, output column wn*64 + 32 j + lane % 32.  Quantised
-// weights (QS): the per-128-output scales multiply the sums here.
-template <int MODE, int NG, bool QS>
+// row arow0 + RS i + lane % 32; DOWN*: acc[i][j] holds activation row
+// arow0 + RS i + R, output column wn*64 + 32 j + lane % 32.  Quantised
+// weights (QS): the per-128-output scales multiply the sums here.  BNB:
+// weight rows of the tile (output columns of a partial-tile slab row).
+template <int MODE, int NG, bool QS, int RS = 64, int BNB = 256>
 __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)[NG][2],
                                               const TileMap& t, int arow0, int n0, int wn) {
   const int lane = threadIdx.x & 63;
@@ -913,7 +930,7 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const int m = t.m0 + arow0 + i * 64 + ccol;
+      const int m = t.m0 + arow0 + i * RS + ccol;
       if (m >= t.rows) continue;
       uint16_t* hrow = p.H + (hbase + m) * p.h_ld;
 #pragma unroll
@@ -921,10 +938,10 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
         const int n = n0 + wn * 32 + q * 8 + rbase;  // 4 consecutive hidden columns
         if (n >= N) continue;
         if (t.slab >= 0) {  // piece of a split tail tile: gate and up partial sums
-          float* sl = p.tail_slab + (int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0);
+          float* sl = p.tail_slab + (int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * BNB + (n - n0);
           *(float4*)sl = make_float4(acc[i][0][q * 4] * sg, acc[i][0][q * 4 + 1] * sg,
                                      acc[i][0][q * 4 + 2] * sg, acc[i][0][q * 4 + 3] * sg);
-          *(float4*)(sl + 128) = make_float4(acc[i][1][q * 4] * su, acc[i][1][q * 4 + 1] * su,
+          *(float4*)(sl + BNB / 2) = make_float4(acc[i][1][q * 4] * su, acc[i][1][q * 4 + 1] * su,
                                              acc[i][1][q * 4 + 2] * su, acc[i][1][q * 4 + 3] * su);
           continue;
         }
@@ -953,7 +970,7 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = t.m0 + arow0 + i * 64 + q * 8 + rbase + r;
+          const int m = t.m0 + arow0 + i * RS + q * 8 + rbase + r;
           if (m >= t.rows) continue;
           float wgt = 1.f;
           int64_t orow;
@@ -976,7 +993,7 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
             if (MODE == MODE_DOWN)
               atomicAdd(&p.y[orow * N + n], wgt * v);
             else if (t.slab >= 0)
-              p.tail_slab[(int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * 256 + (n - n0)] = v;
+              p.tail_slab[(int64_t)t.slab * p.slab_piece + (int64_t)(m - t.m0) * BNB + (n - n0)] = v;
             else
               p.y_perm[orow * N + n] = v;
           }
@@ -987,30 +1004,43 @@ __device__ __forceinline__ void store_tile_pp(const GemmParams& p, f32x16 (&acc)
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong kernel: 256 x 256 tiles, 512 threads = 8 waves, two per SIMD
-// (wave w runs on SIMD w % 4).  Wave w computes 128 activation rows (the
-// 32-row granules (w & 1) + 2i) x 64 weight rows (quarter w >> 1; in
-// MODE_GATEUP 32 rows of W1 and the same 32 rows of W3).  Each wave
-// alternates a read phase (the fragments of one 32-deep K slice, LDS ->
+// Ping-pong kernel: 512 threads = 8 waves, two per SIMD (wave w runs on SIMD
+// w % 4), over 256 x 256 tiles or (BMT = 128) tiles of 128 activation rows x
+// 512 weight rows.  256-row tiles: wave w computes 128 activation rows (the
+// 32-row granules (w & 1) + 2i) x 64 weight rows (quarter w >> 1); 128-row
+// tiles: all four granules x 64 weight rows (eighth w).  In MODE_GATEUP a
+// wave's 64 weight rows are 32 rows of W1 and the same 32 rows of W3.  Each
+// wave alternates a read phase (the fragments of one 32-deep K slice, LDS ->
 // registers; 8-bit weight codes are widened exactly to bf16 here) and a
 // compute phase (16 MFMAs 32x32x16 on them); waves 4..7 run one phase behind
 // waves 0..3, so on every SIMD one wave's MFMAs issue back to back while the
 // other's LDS reads and conversions are in flight.  A barrier separates the
 // phases.  Operands move global -> LDS by buffer_load ... lds into NS stages
-// of 64-deep steps (the XOR-swizzled row layout of DmaCfg): waves 0..3 fetch
-// the weight tile of step s + NS - 1 during their read of slice 2s, waves
-// 4..7 its activation tile one phase later, and each waits for its own loads
-// of a step at the end of the phase before that step is first read.  Tile
-// map, K split and the partial-tile slab are those of grouped_gemm_dma_kernel.
-template <int MODE, int WQ, int NS>
+// of 64-deep steps (the XOR-swizzled row layout of DmaCfg).  256-row tiles:
+// waves 0..3 fetch the weight tile, waves 4..7 the activation tile; 128-row
+// tiles: every wave fetches 64 weight rows and 16 activation rows.  A wave
+// issues its loads of step s + NS - 1 during its read of slice 2s (waves
+// 4..7 one phase after waves 0..3) and waits for its own loads of a step at
+// the end of the phase before that step is first read.  Tile map, K split,
+// K rotation and the partial-tile slab are those of grouped_gemm_dma_kernel.
+// The 128 x 512 shape serves experts of about 128 rows (a 256-row tile would
+// be half empty): per MFMA it moves fewer operand bytes into LDS and widens
+// fewer weight codes.
+template <int MODE, int WQ, int NS, int BMT = 256>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   static_assert(WQ == WQ_BF16 || WQ == WQ_FP8 || WQ == WQ_INT8, "bf16 or 8-bit weights");
+  static_assert(BMT == 256 || BMT == 128, "activation tile rows");
   constexpr bool QW = WQ != WQ_BF16;  // weight codes with scales
   constexpr int WBITS = wq_bits(WQ);
-  using C = DmaCfg<64, NS, WBITS, 256>;
-  constexpr int BNB = 256;
+  constexpr bool WIDE = BMT == 128;
+  constexpr int BNB = WIDE ? 512 : 256;  // weight rows of the tile
+  using C = DmaCfg<64, NS, WBITS, BMT, BNB>;
   constexpr int NT = 512;
-  constexpr int NIB = 64 / C::ROWS_PER_INST_B;  // B DMA instructions per wave and step
+  constexpr int NIB = 64 / C::ROWS_PER_INST_B;   // B DMA instructions per loading wave and step
+  constexpr int AROWS = WIDE ? 16 : 64;          // activation rows per loading wave
+  constexpr int NIA = AROWS / C::ROWS_PER_INST;  // A DMA instructions per loading wave and step
+  constexpr int NV = WIDE ? NIB + NIA : (NIB > NIA ? NIB : NIA);  // most per wave and step
+  constexpr int RS = WIDE ? 32 : 64;             // activation rows between a wave's granules
   extern __shared__ __attribute__((aligned(1024))) char dlds[];
   if (p.zero_out) {  // every workgroup clears its share, with or without a tile
     const int64_t n4 = p.zero_n / 4;
@@ -1019,7 +1049,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < p.zero_n - n4 * 4) p.zero_out[n4 * 4 + threadIdx.x] = 0.f;
   }
   TileMap t;
-  if (!map_tile<MODE, 256, NT>(p, t)) return;
+  if (!map_tile<MODE, BMT, NT>(p, t)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1033,47 +1063,69 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   const int64_t ebytes = (int64_t)N * KW * WBITS / 8;
   const int64_t eoff = t.shared_e ? 0 : (int64_t)t.e * ebytes;
 
-  // ---- DMA: wave widx of group 0 loads B tile rows widx*64 .. +64 (in
-  // MODE_GATEUP waves 0, 1 rows of W1, waves 2, 3 the same rows of W3), of
-  // group 1 the A tile rows widx*64 .. +64; an instruction fills 1 KiB.
-  const bool b_loader = grp == 0;
-  const bool w3 = (MODE == MODE_GATEUP) && b_loader && widx >= 2;
+  // ---- DMA.  The wave's weight rows brow0 .. +64 of the B tile (MODE_GATEUP:
+  // the first half of the tile's rows are W1 rows, the second half the same
+  // rows of W3) and activation rows arow_ld .. +AROWS of the A tile; an
+  // instruction fills 1 KiB.
+  const bool b_loader = WIDE || grp == 0;
+  const bool a_loader = WIDE || grp == 1;
+  const int brow0 = (WIDE ? wave : widx) * 64;
+  const int arow_ld = (WIDE ? wave : widx) * AROWS;
+  const bool w3 = (MODE == MODE_GATEUP) && brow0 >= BNB / 2;
   const void* bsrc = w3 ? (t.shared_e ? p.B1s : p.B1) : (t.shared_e ? p.B0s : p.B0);
-  const __amdgpu_buffer_rsrc_t rsW = uniform_rsrc(
-      b_loader ? (const char*)bsrc + eoff : (const char*)p.A, b_loader ? ebytes : p.A_bytes);
+  const __amdgpu_buffer_rsrc_t rsB = uniform_rsrc((const char*)bsrc + eoff, ebytes);
+  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A, p.A_bytes);
   constexpr uint32_t kOobOff = 0x80000000u;
-  uint32_t voff[8];
+  uint32_t voffb[NIB], voffa[NIA];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (b_loader) {
-      const int r = widx * 64 + j * C::ROWS_PER_INST_B + lane / C::CPRB;  // tile row, 0..255
-      const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
-      const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
-      voff[j] = (j < NIB && n < N) ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
-    } else {
-      const int r = widx * 64 + j * C::ROWS_PER_INST + lane / C::CPR;
-      const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
-      const int m = t.m0 + r;
-      voff[j] = m < t.rows ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16)
-                           : kOobOff;
-    }
+  for (int j = 0; j < NIB; ++j) {
+    const int r = brow0 + j * C::ROWS_PER_INST_B + lane / C::CPRB;  // tile row, 0 .. BNB-1
+    const int chunk = (lane % C::CPRB) ^ ((r / C::RPSB) % C::CPRB);
+    const int n = (MODE == MODE_GATEUP) ? n0 + (r & (BNB / 2 - 1)) : n0 + r;
+    voffb[j] = n < N ? (uint32_t)((int64_t)n * KW * WBITS / 8 + chunk * 16) : kOobOff;
   }
-  // activation instructions whose 8 rows all lie past the segment's end are
-  // not issued (a prefix of the wave's 8 is)
-  const int n_inst = b_loader ? NIB
-                              : __builtin_amdgcn_readfirstlane(
-                                    max(0, min(8, (t.rows - t.m0 - widx * 64 + 7) / 8)));
+#pragma unroll
+  for (int j = 0; j < NIA; ++j) {
+    const int r = arow_ld + j * C::ROWS_PER_INST + lane / C::CPR;
+    const int chunk = (lane % C::CPR) ^ ((r / C::RPS) % C::CPR);
+    const int m = t.m0 + r;
+    voffa[j] = m < t.rows ? (uint32_t)((a_row<MODE>(p, t, m) * K + kbeg_el) * 2 + chunk * 16)
+                          : kOobOff;
+  }
+  // activation instructions whose rows all lie past the segment's end are
+  // not issued (a prefix of the wave's NIA is)
+  const int n_inst_a = a_loader ? __builtin_amdgcn_readfirstlane(max(
+                                      0, min(NIA, (t.rows - t.m0 - arow_ld + C::ROWS_PER_INST - 1) /
+                                                      C::ROWS_PER_INST)))
+                                : 0;
+  const int per_step = (b_loader ? NIB : 0) + n_inst_a;  // the wave's loads per step
+  // K rotation: the workgroup walks its K steps from a start of its own
+  // (concurrent workgroups then stream different offsets of their rows)
+  const int krot = p.krot ? __builtin_amdgcn_readfirstlane(
+                                (int)(((uint32_t)blockIdx.x * (uint32_t)p.krot) % (uint32_t)max(nk, 1)))
+                          : 0;
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    char* dst = dlds + (kt % NS) * C::STAGE_BYTES +
-                (b_loader ? C::TILE_BYTES + widx * 64 * C::RBB : widx * 64 * C::RB);
-    int kb = kbeg_st + kt;
+    char* sbase = dlds + (kt % NS) * C::STAGE_BYTES;
+    const int kr = kt + krot < nk ? kt + krot : kt + krot - nk;
+    int kb = kbeg_st + kr;
     kb = kb >= nkw ? kb - nkw : kb;
-    const int soff = __builtin_amdgcn_readfirstlane(b_loader ? kb * C::RBB : kt * C::RB);
-    static_for<8>([&](auto j) {
-      if (j < n_inst)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(dst + j * 1024), 16, voff[j], soff,
+    if (b_loader) {
+      char* dst = sbase + C::TILE_BYTES + brow0 * C::RBB;
+      const int soff = __builtin_amdgcn_readfirstlane(kb * C::RBB);
+      static_for<NIB>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j], soff,
                                                  0, 1);
-    });
+      });
+    }
+    if (a_loader) {
+      char* dst = sbase + arow_ld * C::RB;
+      const int soff = __builtin_amdgcn_readfirstlane(kr * C::RB);
+      static_for<NIA>([&](auto j) {
+        if (j < n_inst_a)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)(dst + j * 1024), 16, voffa[j],
+                                                   soff, 0, 1);
+      });
+    }
   };
   // "every load of step u has landed": the loads of the later steps issued
   // so far (up to step min(u + NS - 2, nk - 1)) may stay in flight
@@ -1081,14 +1133,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
     const int later = min(u + NS - 2, nk - 1) - u;
     if (NS == 2 || later <= 0)
       wait_vmcnt<0>();
-    else if (b_loader)
-      wait_vmcnt_dyn<8 * (NS - 2)>(later * NIB);
     else
-      wait_vmcnt_dyn<8 * (NS - 2)>(later * n_inst);
+      wait_vmcnt_dyn<NV * (NS - 2)>(later * per_step);
   };
 
   // ---- the wave's tile
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = WIDE ? 0 : (wave & 1), wn = WIDE ? wave : (wave >> 1);
   const int frow = lane & 31, fhalf = lane >> 5;
   const int swz = (frow / C::RPS) % C::CPR;     // fragment rows are 32-aligned + frow
   const int swzb = (frow / C::RPSB) % C::CPRB;
@@ -1096,8 +1146,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
   int b_row[2];
   b_row[0] = (MODE == MODE_GATEUP) ? wn * 32 + frow : wn * 64 + frow;
   b_row[1] = (MODE == MODE_GATEUP) ? BNB / 2 + wn * 32 + frow : wn * 64 + 32 + frow;
-  const int vg = min(8, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
-  const int ng = __builtin_amdgcn_readfirstlane(vg > wm ? (vg - wm + 1) / 2 : 0);
+  const int vg = min(BMT / 32, (t.rows - t.m0 + 31) / 32);  // valid granules of the tile
+  const int ng = __builtin_amdgcn_readfirstlane(WIDE ? vg : (vg > wm ? (vg - wm + 1) / 2 : 0));
 
   if (nk <= 0) return;  // (every unit of the schedule has at least one step)
   // prologue: steps 0 .. NS - 2 in flight, wait for step 0
@@ -1139,7 +1189,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
           const int co = ((((sl & 1) * 4 + kk * 2 + fhalf) ^ swz) * 16);
 #pragma unroll
           for (int i = 0; i < NG; ++i)
-            fa[kk][i] = *(const bf16x8*)(a + (arow0 + i * 64 + frow) * C::RB + co);
+            fa[kk][i] = *(const bf16x8*)(a + (arow0 + i * RS + frow) * C::RB + co);
           if constexpr (!QW) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) fq[kk][j] = *(const bf16x8*)(b + b_row[j] * C::RBB + co);
@@ -1190,7 +1240,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
       bar();
     }
     if (grp == 0) bar();
-    if constexpr (NG > 0) store_tile_pp<MODE, NG, QW>(p, acc, t, arow0, n0, wn);
+    if constexpr (NG > 0) store_tile_pp<MODE, NG, QW, RS, BNB>(p, acc, t, arow0, n0, wn);
   };
   if (ng >= 4)
     run(std::integral_constant<int, 4>{});
@@ -1422,14 +1472,17 @@ hipError_t launch_gemm_dma(const GemmParams& p0, hipStream_t st) {
 
 
 
-// The ping-pong kernel (256-row tiles): 512 threads, NS 64-deep stages
-// (bf16 weights: two of 64 KiB; 8-bit weights: three of 48 KiB).
-template <int MODE, int WQ, int NS>
+// The ping-pong kernel: 512 threads, NS 64-deep stages (256 x 256 tiles:
+// bf16 weights two stages of 64 KiB, 8-bit weights three of 48 KiB; 128 x 512
+// tiles, 8-bit weights only: three stages of 48 KiB).  The 128 x 512 shape
+// takes no K split of tail tiles.
+template <int MODE, int WQ, int NS, int BMT = 256>
 hipError_t launch_gemm_pp(const GemmParams& p0, hipStream_t st) {
   if (p0.mt_max <= 0 || p0.nt <= 0) return hipSuccess;
-  using C = DmaCfg<64, NS, wq_bits(WQ), 256>;
+  constexpr int BNB = BMT == 128 ? 512 : 256;
+  using C = DmaCfg<64, NS, wq_bits(WQ), BMT, BNB>;
   constexpr size_t kLds = C::LDS;
-  const void* kern = (const void*)grouped_gemm_pp_kernel<MODE, WQ, NS>;
+  const void* kern = (const void*)grouped_gemm_pp_kernel<MODE, WQ, NS, BMT>;
   static KernelSlots ks;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -1448,13 +1501,19 @@ hipError_t launch_gemm_pp(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.kunit = 64 / BK;
   p.slots = slots;
-  p.slab_piece = 256 * 256;
-  p.krot = 0;
+  p.slab_piece = BMT * BNB;
+  if (WQ == WQ_BF16 || !MOE_PP_KROT) p.krot = 0;
+  if (BMT != 256) {
+    // weight tiles of the wider shape; no tail split (the fixup pass sums
+    // 256-column pieces)
+    p.nt = (MODE == MODE_GATEUP) ? (p.N + BNB / 2 - 1) / (BNB / 2) : (p.N + BNB - 1) / BNB;
+    p.split_max = 1;
+  }
   constexpr bool slab_mode = (MODE == MODE_DOWN_PERM || MODE == MODE_GATEUP);
   if (slab_mode && (!p.tail_slab || (int64_t)kNumXcd * slots * p.slab_piece > p.slab_floats))
     p.split_max = 1;
-  p.mt_max = (int)((p.P_max + 255) / 256 + p.E + (p.has_shared ? (p.T + 255) / 256 : 0));
-  grouped_gemm_pp_kernel<MODE, WQ, NS><<<sched_grid(p), 512, kLds, st>>>(p);
+  p.mt_max = (int)((p.P_max + BMT - 1) / BMT + p.E + (p.has_shared ? (p.T + BMT - 1) / BMT : 0));
+  grouped_gemm_pp_kernel<MODE, WQ, NS, BMT><<<sched_grid(p), 512, kLds, st>>>(p);
   if (slab_mode && p.split_max > 1)
     tail_fixup_kernel<MODE, 256><<<(unsigned)(kNumXcd * std::max(1, slots / 2) * kFixBands), 256, 0,
                                    st>>>(p);
@@ -1479,18 +1538,27 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
     // bf16 weights at 16 or fewer rows per expert: 32-row tiles with two
     // 64-deep stages, two workgroups per CU (decode at 16 rows per expert
     // 0.576 -> 0.542 ms)
-    if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 32, MOE_DECODE_PF>(p, st);
+    if (rows <= 16) return launch_gemm_dma<MODE, WQ_BF16, 64, MOE_DECODE_NS, 32, MOE_DECODE_PF>(p, st);
     return launch_gemm_dma<MODE, WQ_BF16, 32, 3, 64>(p, st);
   }
-  // 8-bit weights: the ping-pong kernel when experts fill whole 256-row
-  // tiles; with fewer rows its phases are short and their barriers dominate
-  // (measured on the 256-expert layer, about 128 rows per expert: fp8 6.41 ms
-  // with the four-wave kernel against 7.26 ms)
+  // 8-bit weights: the ping-pong kernel on 256 x 256 tiles when experts fill
+  // whole 256-row tiles; with about 128 rows per expert the half-empty
+  // tiles make its phases short and their barriers dominate (measured on the
+  // 256-expert layer: fp8 6.41 ms with the four-wave kernel against 7.26 ms).
+  // There its 128 x 512 shape keeps the phases full: the down projection
+  // 2.75 -> 2.46 ms (fp8), 2.87 -> 2.64 ms (int8); not the gate/up
+  // projection (3.55 -> 4.0 ms), which keeps the four-wave kernel
+  // (MOE_PP8_WIDE: bit 1 << MODE per launch)
   const bool pp8 = MOE_GEMM_PP && rows >= MOE_PP8_ROWS;
+  const bool pp8w = MOE_GEMM_PP && ((MOE_PP8_WIDE >> MODE) & 1) && !pp8;
   if (wq == WQ_FP8)
-    return pp8 ? launch_gemm_pp<MODE, WQ_FP8, 3>(p, st) : launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
+    return pp8    ? launch_gemm_pp<MODE, WQ_FP8, 3>(p, st)
+           : pp8w ? launch_gemm_pp<MODE, WQ_FP8, 3, 128>(p, st)
+                  : launch_gemm_dma<MODE, WQ_FP8, 64, 2>(p, st);
   if (wq == WQ_INT8)
-    return pp8 ? launch_gemm_pp<MODE, WQ_INT8, 3>(p, st) : launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
+    return pp8    ? launch_gemm_pp<MODE, WQ_INT8, 3>(p, st)
+           : pp8w ? launch_gemm_pp<MODE, WQ_INT8, 3, 128>(p, st)
+                  : launch_gemm_dma<MODE, WQ_INT8, 64, 2>(p, st);
   if (wq == WQ_INT4) return launch_gemm_dma<MODE, WQ_INT4, 64, 2>(p, st);
   if (MOE_GEMM_PP) return launch_gemm_pp<MODE, WQ_BF16, 2>(p, st);
   return launch_gemm_dma<MODE, WQ_BF16, 64, 2, 256, MOE_GEMM_PF>(p, st);

@@ -49,3 +49,38 @@ def test_roofline_floors_of_the_workloads():
     # an expert the step never touched costs no weight bytes
     f = bench.roofline_floor(CONFIGS["capacity_skew"], [640] * 30 + [0] * 34, 640 * 30)
     assert f["touched_experts"] == 30
+
+
+def test_gemm_kernel_named_for_each_workload():
+    """The expert GEMM kernel bench.py names: the ping-pong kernel at the
+    Mixtral shape (1024 rows per expert) and for the bf16 256-expert layer
+    (128 rows); for its fp8 variant (128 rows, under the 256-row threshold)
+    the four-wave kernel in the gate/up projection and the ping-pong kernel's
+    128 x 512 tiles in the down projection; the four-wave kernel for int4,
+    decode-sized tiles at 16 rows."""
+    import bench
+    from moe_synth.configs import CONFIGS
+    assert bench.gemm_kernel(CONFIGS["mixtral"], -1) == "grouped_gemm_pp_kernel"
+    assert bench.gemm_kernel(CONFIGS["fine_grained"], -1) == "grouped_gemm_pp_kernel"
+    assert bench.gemm_kernel(CONFIGS["fine_grained_fp8"], -1) == "grouped_gemm_dma_kernel"
+    assert bench.gemm_kernel(CONFIGS["fine_grained_fp8"], -1, "down") == \
+        "grouped_gemm_pp_kernel (128 x 512 tiles)"
+    assert bench.gemm_kernel(CONFIGS["fine_grained_int4"], -1) == "grouped_gemm_dma_kernel"
+    assert bench.gemm_kernel(CONFIGS["decode"], -1).startswith("grouped_gemm_dma_kernel (decode")
+    c = CONFIGS["capacity_skew"]
+    assert bench.gemm_kernel(c, 640) == "grouped_gemm_pp_kernel"
+
+
+def test_gate_up_bytes_of_the_decode_step():
+    """The decode step's gate/up launch moves W1 and W3 of the 8 touched
+    experts (8 * 2 * 4096 * 14336 bf16 = 1.879 GB), the 128 gathered x rows
+    and the 128 hidden rows it writes; fp8 codes halve the weights and add
+    one fp32 scale per 128 rows."""
+    import bench
+    from moe_synth.configs import CONFIGS
+    c = CONFIGS["decode"]
+    w = 8 * 2 * 4096 * 14336 * 2
+    assert bench.gate_up_bytes(c, [16] * 8) == w + 128 * 4096 * 2 + 128 * 14336 * 2
+    assert bench.gate_up_bytes(c, [32] * 4 + [0] * 4) == w // 2 + 128 * 4096 * 2 + 128 * 14336 * 2
+    f = CONFIGS["decode_fp8"]
+    assert bench.gate_up_bytes(f, [16] * 8) == w // 2 + 8 * 2 * 112 * 4 + 128 * 4096 * 2 + 128 * 14336 * 2

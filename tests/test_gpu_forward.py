@@ -43,7 +43,8 @@ SMALL = [
     (64, 512, 8, 2, 1408, None, False, "fp8_e4m3", None),
     (48, 256, 4, 2, 256, None, True, "bf16", None),
     (96, 256, 16, 2, 384, 0.75, True, "fp8_e4m3", "zipf1.5"),
-    # fp8 weights with 256-row tiles (the LDS-DMA kernel's fp8 path)
+    # fp8 weights with 256 or more rows per expert (the ping-pong kernel's
+    # 256 x 256 tiles)
     (1100, 512, 8, 2, 384, None, True, "fp8_e4m3", None),
     (2000, 256, 4, 2, 256, 1.0, False, "fp8_e4m3", "zipf1.5"),
     # long down-projection K with few tiles per XCD: every tile is a split
@@ -53,7 +54,14 @@ SMALL = [
     # long gate/up K (d = 4096) with few tiles: every gate/up tile is split,
     # its gate and up partial sums finished (SwiGLU) by the fixup pass
     (300, 4096, 4, 2, 256, None, True, "bf16", None),
+    (600, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
+    # 8-bit weights with 33..255 rows per expert: the ping-pong kernel's
+    # 128 x 512 tiles (ragged row tiles, a shared expert's partial tiles,
+    # partial weight tiles in both projections, a long K)
     (300, 4096, 4, 2, 256, None, False, "fp8_e4m3", None),
+    (700, 768, 8, 2, 384, None, True, "fp8_e4m3", None),
+    (600, 512, 8, 2, 640, None, True, "int8", None),
+    (160, 256, 4, 2, 256, 1.0, False, "int8", "zipf1.5"),
     # the largest expert counts: 512 and 1024 experts (16 expert blocks in
     # the router, 1024 segments in the GEMM schedule)
     (700, 256, 512, 4, 128, None, False, "bf16", None),

@@ -78,6 +78,9 @@
 #ifndef MOE_PP_KROT
 #define MOE_PP_KROT 1
 #endif
+#ifndef MOE_B_NT_MAX
+#define MOE_B_NT_MAX 256
+#endif
 #ifndef MOE_DECODE_NS
 #define MOE_DECODE_NS 2
 #endif
@@ -138,6 +141,7 @@ struct GemmParams {
   int group_n;                // weight tiles per expert-aligned block of the tile order
   int nfast;                  // tile order inside a block: weight tiles fastest (1) or row tiles
   int krot;                   // K walk start of workgroup b: (b * krot) mod (its K steps); 0 = none
+  int b_nt;                   // weight loads as non-temporal (each weight panel read by one row tile)
   float* zero_out;            // zero_n floats (16-byte aligned) the workgroups clear first, or NULL
   int64_t zero_n;             //   (the atomic combine's y, cleared by the gate/up launch)
 };
@@ -435,6 +439,11 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 // fragment reads of 32 consecutive rows hit distinct banks while each
 // wave-level DMA instruction still writes 1 KiB contiguously.
 constexpr int DMA_BM = 256;
+// cache policy of a DMA load (the buffer instruction's aux operand): 1 for the
+// operand panels that tiles share through L2, kAuxStream (the non-temporal
+// bit) for weight panels that only one row tile reads, which then do not
+// push the shared activation rows out of L2
+constexpr int kAuxStream = 2;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int KB, int NS, int WBITS, int BMA = 256, int BNT = 256>
@@ -669,14 +678,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     kb = kb >= nkw ? kb - nkw : kb;
     const int soff = __builtin_amdgcn_readfirstlane(a_wave ? kr * C::RB : kb * C::RBB);
     if constexpr (C::NI == C::NIB) {
-      static_for<C::NI>([&](auto j) {
-        if (j < a_valid)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
-      });
+      if (!a_wave && p.b_nt)
+        static_for<C::NIB>([&](auto j) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
+        });
+      else
+        static_for<C::NI>([&](auto j) {
+          if (j < a_valid)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+        });
     } else if (a_wave) {
       static_for<C::NI>([&](auto j) {
         if (j < a_valid)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
+      });
+    } else if (p.b_nt) {
+      static_for<C::NIB>([&](auto j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
       });
     } else {
       static_for<C::NIB>([&](auto j) {
@@ -1112,10 +1130,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
     if (b_loader) {
       char* dst = sbase + C::TILE_BYTES + brow0 * C::RBB;
       const int soff = __builtin_amdgcn_readfirstlane(kb * C::RBB);
-      static_for<NIB>([&](auto j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j], soff,
-                                                 0, 1);
-      });
+      if (p.b_nt)
+        static_for<NIB>([&](auto j) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j],
+                                                   soff, 0, kAuxStream);
+        });
+      else
+        static_for<NIB>([&](auto j) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j],
+                                                   soff, 0, 1);
+        });
     }
     if (a_loader) {
       char* dst = sbase + arow_ld * C::RB;
@@ -1548,7 +1572,9 @@ hipError_t launch_gemm(int wq, int64_t rows, const GemmParams& p, hipStream_t st
   // There its 128 x 512 shape keeps the phases full: the down projection
   // 2.75 -> 2.46 ms (fp8), 2.87 -> 2.64 ms (int8); not the gate/up
   // projection (3.55 -> 4.0 ms), which keeps the four-wave kernel
-  // (MOE_PP8_WIDE: bit 1 << MODE per launch)
+  // (MOE_PP8_WIDE: bit 1 << MODE per launch).  For that kernel, 128-row
+  // activation tiles (two, three or four stages) and three stages of 256
+  // rows measured slower (3.63 -> 4.9..5.2 and 3.9 ms)
   const bool pp8 = MOE_GEMM_PP && rows >= MOE_PP8_ROWS;
   const bool pp8w = MOE_GEMM_PP && ((MOE_PP8_WIDE >> MODE) & 1) && !pp8;
   if (wq == WQ_FP8)
@@ -1676,6 +1702,15 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // 256-expert layer: 5-6% faster for fp8 and int8, neutral for int4, slower
   // for bf16 weights and for decode-sized batches)
   g.krot = (!deep && (wq == WQ_FP8 || wq == WQ_INT8)) ? 7 : 0;
+  // bf16 weight panels read by a single row tile (experts of at most one
+  // 256-row tile on average): their loads stream past L2.  Measured: the
+  // 256-expert layer 5.94 -> 5.72 ms, decode at 16 rows per expert 0.525 ->
+  // 0.485 ms; with four row tiles per expert (the Mixtral-shaped layer) 2.5%
+  // slower.  Not for 8-bit or 4-bit codes: a 64-deep step reads only part of
+  // each 128-byte line, and the next step finds the rest in L2 only if the
+  // line stayed (fp8 256-expert layer 6.14 -> 7.35 ms, decode 0.32 -> 0.43 ms
+  // with the streaming hint)
+  g.b_nt = (wq == WQ_BF16 && rows_avg <= MOE_B_NT_MAX) ? 1 : 0;
   hipError_t err = launch_gemm<MODE_GATEUP>(wq, rows_avg, g, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {

@@ -215,15 +215,38 @@ def test_T0_is_a_noop(moe):
 
 
 def test_determinism_k2(moe):
+    """The fused (atomic) combine with k = 2 and an unsplit down projection
+    (d_ff = 256: one K piece per tile): every y element receives two fp32
+    adds onto zero, which commute, so two runs are bit-identical."""
     cfg = custom_config(900, 512, 8, 2, 256, seed=77)
     wl = Workload(cfg)
-    out1, layer, dev = gpu_forward(wl)
+    out1, layer, dev = gpu_forward(wl, combine="fused")
     layer(dev["x"])
     torch.cuda.synchronize()
     assert np.array_equal(layer.topk_idx.cpu().numpy(), out1["idx"])
     assert np.array_equal(layer.topk_w.cpu().numpy(), out1["w"])
-    # zero + two fp32 atomic adds commute: y is bit-identical for k = 2
     assert np.array_equal(layer.y.cpu().numpy(), out1["y"])
+
+
+def test_decode_sized_reproducibility(moe):
+    """A decode-sized batch with a long down-projection K (d_ff = 4096): the
+    fused combine splits each down tile over K, so a y element receives
+    k * pieces fp32 atomic adds in an order that can change between runs
+    (two runs agree within the tolerance, not necessarily bit for bit); the
+    grouped combine sums the pieces and the rows in a fixed order, so two
+    runs are bit-identical."""
+    cfg = custom_config(64, 1024, 8, 2, 4096, seed=78)
+    wl = Workload(cfg)
+    out_g, layer_g, dev = gpu_forward(wl, combine="grouped")
+    layer_g(dev["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(layer_g.y.cpu().numpy(), out_g["y"])
+    out_f, layer_f, _ = gpu_forward(wl, combine="fused", dev=dev)
+    layer_f(dev["x"])
+    torch.cuda.synchronize()
+    assert rel_err(layer_f.y.cpu().numpy(), out_f["y"]) < 1e-5
+    assert rel_err(out_f["y"], out_g["y"]) < 1e-5
+    check_forward(wl, out_f)
 
 
 def _full_size(wl, **kw):

@@ -78,8 +78,8 @@
 #ifndef MOE_PP_KROT
 #define MOE_PP_KROT 1
 #endif
-#ifndef MOE_B_NT_MAX
-#define MOE_B_NT_MAX 256
+#ifndef MOE_B_NT
+#define MOE_B_NT 1
 #endif
 #ifndef MOE_DECODE_NS
 #define MOE_DECODE_NS 2
@@ -141,7 +141,8 @@ struct GemmParams {
   int group_n;                // weight tiles per expert-aligned block of the tile order
   int nfast;                  // tile order inside a block: weight tiles fastest (1) or row tiles
   int krot;                   // K walk start of workgroup b: (b * krot) mod (its K steps); 0 = none
-  int b_nt;                   // weight loads as non-temporal (each weight panel read by one row tile)
+  int b_nt;                   // weight loads of a tile whose expert fits in that one row tile
+                              // (so no other tile reads its weight panel) as non-temporal
   float* zero_out;            // zero_n floats (16-byte aligned) the workgroups clear first, or NULL
   int64_t zero_n;             //   (the atomic combine's y, cleared by the gate/up launch)
 };
@@ -661,6 +662,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     return __builtin_amdgcn_readfirstlane(
         max(0, min(C::NI, (left + C::ROWS_PER_INST - 1) / C::ROWS_PER_INST)));
   }();
+  // the weight panel of an expert that fits in this one row tile is read by
+  // this workgroup only: its loads may stream past L2
+  const bool b_nt = p.b_nt && t.rows <= BMA;
   // K rotation: the workgroup walks its K steps from a start of its own, so
   // concurrent workgroups streaming rows of the same pitch (a power of two
   // in the usual shapes) do not all address the same offset within their
@@ -678,7 +682,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     kb = kb >= nkw ? kb - nkw : kb;
     const int soff = __builtin_amdgcn_readfirstlane(a_wave ? kr * C::RB : kb * C::RBB);
     if constexpr (C::NI == C::NIB) {
-      if (!a_wave && p.b_nt)
+      if (!a_wave && b_nt)
         static_for<C::NIB>([&](auto j) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
         });
@@ -692,7 +696,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
         if (j < a_valid)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
-    } else if (p.b_nt) {
+    } else if (b_nt) {
       static_for<C::NIB>([&](auto j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
       });
@@ -1117,6 +1121,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
                                                       C::ROWS_PER_INST)))
                                 : 0;
   const int per_step = (b_loader ? NIB : 0) + n_inst_a;  // the wave's loads per step
+  // the weight panel of an expert that fits in this one row tile is read by
+  // this workgroup only: its loads may stream past L2
+  const bool b_nt = p.b_nt && t.rows <= BMT;
   // K rotation: the workgroup walks its K steps from a start of its own
   // (concurrent workgroups then stream different offsets of their rows)
   const int krot = p.krot ? __builtin_amdgcn_readfirstlane(
@@ -1130,7 +1137,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
     if (b_loader) {
       char* dst = sbase + C::TILE_BYTES + brow0 * C::RBB;
       const int soff = __builtin_amdgcn_readfirstlane(kb * C::RBB);
-      if (p.b_nt)
+      if (b_nt)
         static_for<NIB>([&](auto j) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j],
                                                    soff, 0, kAuxStream);
@@ -1702,15 +1709,16 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // 256-expert layer: 5-6% faster for fp8 and int8, neutral for int4, slower
   // for bf16 weights and for decode-sized batches)
   g.krot = (!deep && (wq == WQ_FP8 || wq == WQ_INT8)) ? 7 : 0;
-  // bf16 weight panels read by a single row tile (experts of at most one
-  // 256-row tile on average): their loads stream past L2.  Measured: the
-  // 256-expert layer 5.94 -> 5.72 ms, decode at 16 rows per expert 0.525 ->
-  // 0.485 ms; with four row tiles per expert (the Mixtral-shaped layer) 2.5%
-  // slower.  Not for 8-bit or 4-bit codes: a 64-deep step reads only part of
-  // each 128-byte line, and the next step finds the rest in L2 only if the
-  // line stayed (fp8 256-expert layer 6.14 -> 7.35 ms, decode 0.32 -> 0.43 ms
-  // with the streaming hint)
-  g.b_nt = (wq == WQ_BF16 && rows_avg <= MOE_B_NT_MAX) ? 1 : 0;
+  // bf16 weight panels read by a single row tile (the tile's expert has no
+  // more rows than the tile; decided per tile on the device): their loads
+  // stream past L2.  Measured: the 256-expert layer 5.94 -> 5.72 ms, decode
+  // at 16 rows per expert 0.525 -> 0.485 ms; applied to all tiles of the
+  // Mixtral-shaped layer (four row tiles per expert) 2.5% slower.  Not for
+  // 8-bit or 4-bit codes: a 64-deep step reads only part of each 128-byte
+  // line, and the next step finds the rest in L2 only if the line stayed
+  // (fp8 256-expert layer 6.14 -> 7.35 ms, decode 0.32 -> 0.43 ms with the
+  // streaming hint)
+  g.b_nt = (wq == WQ_BF16 && MOE_B_NT) ? 1 : 0;
   hipError_t err = launch_gemm<MODE_GATEUP>(wq, rows_avg, g, st);
   if (err != hipSuccess) return err;
   if (ev_mid) {

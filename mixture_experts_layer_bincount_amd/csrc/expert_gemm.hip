@@ -681,8 +681,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     int kb = kbeg_st + kr;  // B: the absolute step, wrapped
     kb = kb >= nkw ? kb - nkw : kb;
     const int soff = __builtin_amdgcn_readfirstlane(a_wave ? kr * C::RB : kb * C::RBB);
+    // the streaming hint on the step that reads the last part of each
+    // 128-byte weight line (every step for bf16 rows)
+    const bool nt_now = b_nt && (C::RBB >= 128 || (kb + 1) % (128 / C::RBB) == 0);
     if constexpr (C::NI == C::NIB) {
-      if (!a_wave && b_nt)
+      if (!a_wave && nt_now)
         static_for<C::NIB>([&](auto j) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
         });
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
         if (j < a_valid)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, MOE_AUX);
       });
-    } else if (b_nt) {
+    } else if (nt_now) {
       static_for<C::NIB>([&](auto j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_ptr_t)(gbase + j * 1024), 16, voff[j], soff, 0, kAuxStream);
       });
@@ -1137,7 +1140,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
     if (b_loader) {
       char* dst = sbase + C::TILE_BYTES + brow0 * C::RBB;
       const int soff = __builtin_amdgcn_readfirstlane(kb * C::RBB);
-      if (b_nt)
+      // the streaming hint on the step that reads the last part of each
+      // 128-byte weight line (every step for bf16 rows)
+      if (b_nt && (C::RBB >= 128 || (kb + 1) % (128 / C::RBB) == 0))
         static_for<NIB>([&](auto j) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr_t)(dst + j * 1024), 16, voffb[j],
                                                    soff, 0, kAuxStream);
@@ -1717,7 +1722,8 @@ hipError_t launch_expert_ffn(const moe_shape& s, const WsLayout& L, const moe_we
   // 8-bit or 4-bit codes: a 64-deep step reads only part of each 128-byte
   // line, and the next step finds the rest in L2 only if the line stayed
   // (fp8 256-expert layer 6.14 -> 7.35 ms, decode 0.32 -> 0.43 ms with the
-  // streaming hint)
+  // streaming hint on every step; on the step that reads a line's last part
+  // only, no change either way)
   g.b_nt = (wq == WQ_BF16 && MOE_B_NT) ? 1 : 0;
   hipError_t err = launch_gemm<MODE_GATEUP>(wq, rows_avg, g, st);
   if (err != hipSuccess) return err;

@@ -758,9 +758,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // per-lane LDS byte offsets of the fragment rows (stage 0, chunk slot 0)
   // and of the swizzled 16-byte chunk for each (half, kk) of a step
   const int a_row_off = (arow0 + frow) * C::RB;
+  // 8-bit weight codes (K8): K is permuted within each 32-deep slice so that
+  // a lane's 16 codes of one 16-byte LDS read serve both MFMAs of the slice:
+  // MFMA kk, lane half g takes the 8 K positions 32h + 16g + 8kk + 0..7, and
+  // the activation fragment the same 8 (an 8-byte read per MFMA conflicts
+  // in the LDS banks; the sums are the same up to the order of the adds)
+  constexpr bool K8 = WBITS == 8;
   int col_off[HPS][2];
   static_for<HPS>([&](auto h) {
-    static_for<2>([&](auto kk) { col_off[h][kk] = (((h * 4 + kk * 2 + fhalf) ^ swz) * 16); });
+    static_for<2>([&](auto kk) {
+      col_off[h][kk] = (((h * 4 + (K8 ? fhalf * 2 + kk : kk * 2 + fhalf)) ^ swz) * 16);
+    });
   });
   // quantised weight rows: 8 codes (8 or 4 bytes) per fragment, part of a
   // swizzled 16-byte chunk; the B tile rows are 32-aligned as well
@@ -815,6 +823,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           if constexpr (!FP8) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) fb[kk][j] = *(const bf16x8*)(b + (brow[j] + frow) * C::RB + co);
+          } else if constexpr (K8) {
+            // 16 codes (K 32h + 16 fhalf + 0..15) per lane, read once for both MFMAs
+            if (kk == 0) {
+              const int cb = (((h * 2 + fhalf) ^ swzb) << 4);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint4 q = *(const uint4*)(b + (brow[j] + frow) * C::RBB + cb);
+                fb[0][j] = make_uint2(q.x, q.y);
+                fb[1][j] = make_uint2(q.z, q.w);
+              }
+            }
           } else {
             // the lane's 8 codes: K offset h*32 + kk*16 + fhalf*8 of the step
             const int bo = (h * 32 + kk * 16 + fhalf * 8) * WBITS / 8;
@@ -866,7 +885,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmParams p) 
             }
           }
         });
-        constexpr int NR = 2 * (NG + 4), NM = 8 * NG, MPR = (NM + NR - 1) / NR;
+        constexpr int NR = 2 * NG + (K8 ? 4 : 8), NM = 8 * NG, MPR = (NM + NR - 1) / NR;
         static_for<NR>([&](auto) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);  // MFMAs
@@ -1222,19 +1241,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmParams p) {
         const char* a = dlds + stage * C::STAGE_BYTES;
         const char* b = a + C::TILE_BYTES;
         static_for<2>([&](auto kk) {
-          const int co = ((((sl & 1) * 4 + kk * 2 + fhalf) ^ swz) * 16);
+          // 8-bit codes: K permuted within the slice as in grouped_gemm_dma_kernel
+          // (MFMA kk, lane half g: K positions 32h + 16g + 8kk + 0..7), so one
+          // 16-byte read of codes serves both MFMAs
+          const int co = QW ? (((((sl & 1) * 4 + fhalf * 2 + kk) ^ swz) * 16))
+                            : (((((sl & 1) * 4 + kk * 2 + fhalf) ^ swz) * 16));
 #pragma unroll
           for (int i = 0; i < NG; ++i)
             fa[kk][i] = *(const bf16x8*)(a + (arow0 + i * RS + frow) * C::RB + co);
           if constexpr (!QW) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) fq[kk][j] = *(const bf16x8*)(b + b_row[j] * C::RBB + co);
-          } else {
-            // the lane's 8 codes: K offset (sl & 1) * 32 + kk * 16 + fhalf * 8 of the step
-            const int bo = (sl & 1) * 32 + kk * 16 + fhalf * 8;
-            const int cb = (((bo >> 4) ^ swzb) << 4) + (bo & 15);
+          } else if (kk == 0) {
+            // the lane's 16 codes: K offset (sl & 1) * 32 + fhalf * 16 of the step
+            const int cb = ((((sl & 1) * 2 + fhalf) ^ swzb) << 4);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fq[kk][j] = *(const uint2*)(b + b_row[j] * C::RBB + cb);
+            for (int j = 0; j < 2; ++j) {
+              const uint4 q = *(const uint4*)(b + b_row[j] * C::RBB + cb);
+              fq[0][j] = make_uint2(q.x, q.y);
+              fq[1][j] = make_uint2(q.z, q.w);
+            }
           }
         });
       }
